@@ -1,0 +1,257 @@
+/*
+ * dartree.h - C ABI of the MI355X (gfx950) library for DARTree's depth-wise
+ * batched draft-supertree construction, deferred top-B pruning, the ancestor
+ * attention mask and one tree-attention verification layer.
+ *
+ * Method sources (page title, section):
+ *  [P1] "DARTree: Teaching a Chain-Trained Corrector to Think in Trees"
+ *       (alanhou.org), Core Mechanism and its diagram.
+ *  [P2] "Technische Samenvatting: DARTree" (gist.science), Methodologie,
+ *       part 1 "Depth-Wise Parallel AR Expansie" and part 2 "Deferred
+ *       Best-First Pruning" (Lemma 1).
+ *  [P3] "Accelerating Language Models with Diffusion Draft Trees"
+ *       (legiblepapers), Summary & Methodology Analysis.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or retains them.  Scratch space comes from a
+ *    caller-provided device workspace sized by the matching *_workspace_size.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued on it and the call returns; outputs are valid once the
+ *    caller has synchronised the stream.  Nothing synchronises the host.
+ *  - Arguments are validated on the host before anything is launched.  On an
+ *    error the call returns a negative dt_status, launches nothing and writes
+ *    no output.  Launch failures reported by HIP return DT_EHIP.
+ *  - Results are bitwise reproducible for identical inputs: reductions run in
+ *    a fixed order and no floating-point atomics are used.
+ *  - Calls that share one workspace must not overlap in time.
+ *  - Row-major layouts throughout; "[A][B]" means B is the fastest index.
+ */
+#ifndef DARTREE_H
+#define DARTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DT_OK = 0,
+  DT_EINVAL = -1,       /* a null pointer, a size or a hyper-parameter out of range */
+  DT_EWORKSPACE = -2,   /* workspace null or smaller than *_workspace_size        */
+  DT_EUNSUPPORTED = -3, /* valid by the method but outside this build's limits    */
+  DT_EHIP = -4          /* the HIP runtime reported an error                      */
+} dt_status;
+
+typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
+
+/* Limits of this build (checked on the host). */
+#define DT_MAX_K 16         /* children per branch                              */
+#define DT_MAX_ROWS 256     /* R * W: branch rows evaluated per head call        */
+#define DT_MAX_CAND 4096    /* W * k candidates per request and depth           */
+#define DT_MAX_POOL 8192    /* D * W pool nodes per request                      */
+#define DT_MAX_B 1024       /* verification budget per request                   */
+#define DT_MAX_DEPTH 64
+
+/*
+ * The correction head (read-only, device memory).  The pages fix no head
+ * architecture; this is the synthetic head of the evaluated workloads:
+ *     x  = E[tok] + h_t
+ *     s' = s + GELU(x W1) W2          (exact erf GELU)
+ *     z  = s' U                       (corrected logits)
+ * Storage is output-feature-major so that each weight row is contiguous:
+ *     E   [V][d]      token embedding
+ *     W1t [4d][d]     W1 transposed
+ *     W2t [d][4d]     W2 transposed
+ *     Ut  [V][d]      U transposed (vocab-major: a vocabulary tile is one
+ *                     contiguous block)
+ * wdtype DT_BF16: all four are bfloat16; DT_F32: all four are float32.
+ * d must be a multiple of 128 for DT_BF16 and of 4 for DT_F32.
+ */
+typedef struct {
+  int32_t d;
+  int32_t V;
+  int32_t wdtype;      /* dt_dtype */
+  int32_t reserved;
+  const void* E;
+  const void* W1t;
+  const void* W2t;
+  const void* Ut;
+} dt_head;
+
+/* Human-readable text of a status code (static storage). */
+const char* dartree_status_string(int status);
+
+/* Library version, (major << 16) | minor. */
+int dartree_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Supertree construction                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace build_supertree needs (0 on invalid arguments). */
+size_t build_supertree_workspace_size(const dt_head* head, int R, int D, int W, int k);
+
+/*
+ * build_supertree - depth-wise batched construction of R independent
+ * supertrees that share one correction head ([P1] Core Mechanism; [P2]
+ * part 1; [P3]).
+ *
+ * For t = 1..D, one batched head call runs over every surviving branch of
+ * every request: the state update, the corrected logits z = s'U, the
+ * temperature log-softmax logp = z/T - logsumexp(z/T) and each branch's top-k
+ * children by (logp desc, token asc).  A child's score is its parent's score
+ * plus its logp (accumulated path log-probability).  Per request the best
+ * n_t = min(W, n_{t-1} * k) candidates by (score desc, parent slot asc, child
+ * rank asc) survive and carry their parent's updated state forward; the
+ * child's token enters the next depth's update.  The root (depth 0) is one
+ * branch with state s0, token root_tok and score 0; so n_0 = 1.
+ * T == 0 is the greedy limit: only the lowest-index argmax of z survives as a
+ * child, with logp 0, so each request's supertree is a chain.
+ *
+ * Inputs:
+ *   h         [R][D][d] f32   drafter hidden state for each depth (h[r][t-1]
+ *                             feeds the step producing depth-t tokens)
+ *   s0        [R][d]    f32   root branch state
+ *   root_tok  [R]       i32   last verified token, 0 <= root_tok < V
+ *   1 <= R, 1 <= D <= DT_MAX_DEPTH, 1 <= W, 1 <= k <= min(V, DT_MAX_K),
+ *   R*W <= DT_MAX_ROWS, W*k <= DT_MAX_CAND, D*W <= DT_MAX_POOL, T >= 0 finite.
+ * Outputs (slot j of depth t at index [r][t-1][j]):
+ *   pool_tok    [R][D][W] i32  token, -1 for unused slots
+ *   pool_parent [R][D][W] i32  parent slot at depth t-1; -1 at depth 1 and
+ *                              for unused slots
+ *   pool_score  [R][D][W] f32  accumulated log-probability; -inf if unused
+ *   n_valid     [R][D]    i32  used slots per depth
+ * Slots are in (score desc, parent slot asc, rank asc) order.
+ * Inputs must be finite.
+ */
+int build_supertree(const dt_head* head, const float* h, const float* s0,
+                    const int32_t* root_tok, int R, int D, int W, int k, float T,
+                    int32_t* pool_tok, int32_t* pool_parent, float* pool_score,
+                    int32_t* n_valid, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Stages of one depth (the same kernels build_supertree runs)               */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace for the two stage calls below with `rows` rows. */
+size_t head_step_workspace_size(const dt_head* head, int rows, int k);
+
+/*
+ * state_update - the head's state step for `rows` branches:
+ *   s_out[i] = s_in[i] + GELU((E[tok[i]] + h) W1) W2.
+ *   s_in, s_out [rows][d] f32 (may not alias); tok [rows] i32; h [d] f32.
+ * 1 <= rows <= DT_MAX_ROWS.
+ */
+int state_update(const dt_head* head, const float* s_in, const int32_t* tok,
+                 const float* h, int rows, float* s_out, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/*
+ * corrected_topk - corrected logits z = s U for `rows` states, the temperature
+ * log-softmax over the whole vocabulary and each row's top-k children
+ * ([P1] Core Mechanism: W corrected conditional distributions, top-k each).
+ *   s        [rows][d] f32
+ *   cand_tok [rows][k] i32   tokens by (logp desc, token asc)
+ *   cand_lp  [rows][k] f32   their log-probabilities (T > 0)
+ *   lse      [rows]    f32   logsumexp(z/T) (T > 0); max z when T == 0
+ * With T == 0 only column 0 is meaningful (the lowest-index argmax, lp 0);
+ * the other columns hold token -1 and lp -inf.
+ */
+int corrected_topk(const dt_head* head, const float* s, int rows, int k, float T,
+                   int32_t* cand_tok, float* cand_lp, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Deferred best-first pruning and the verification mask                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * prune_topB - deferred best-first pruning as one global top-B per request
+ * ([P2] part 2, Globale Selectie and Lemma 1; [P3]).
+ *   prio = pool_score + beta * depth (depth 1..D).  The min(B, sum n_valid)
+ *   best valid pool nodes by (prio desc, depth asc, slot asc) are selected and
+ *   emitted in (depth asc, slot asc) order.  For beta <= 0 this set is the
+ *   set a sequential best-first max-heap pops (Lemma 1) and it is
+ *   ancestor-closed, so every emitted parent is emitted earlier.
+ * Inputs: the build_supertree outputs for R requests of D x W slots.
+ *   1 <= B <= min(D*W, DT_MAX_B); beta <= 0 finite (beta > 0 -> DT_EINVAL).
+ * Outputs (row r, entry i < n_sel[r]; entries >= n_sel[r] are -1):
+ *   sel_node   [R][B] i32  flat pool index (t-1)*W + slot
+ *   sel_parent [R][B] i32  index of the parent entry, -1 for depth-1 nodes
+ *   sel_depth  [R][B] i32  depth 1..D
+ *   n_sel      [R]    i32  min(B, number of valid pool nodes)
+ */
+int prune_topB(const float* pool_score, const int32_t* pool_parent,
+               const int32_t* n_valid, int R, int D, int W, int B, float beta,
+               int32_t* sel_node, int32_t* sel_parent, int32_t* sel_depth,
+               int32_t* n_sel, void* stream);
+
+/*
+ * build_tree_mask - ancestor bitmask of each verification tree ([P1] Core
+ * Mechanism: the sparse attention mask lets the target check every branch in
+ * one forward; [P3]: tree-attention mask of the prefix tree).
+ *   mask [R][B][ceil(B/32)] u32: bit (i mod 32) of word (i / 32) of row j is
+ *   set iff entry i is entry j or an ancestor of it.  Rows >= n_sel are zero.
+ *   The verified prefix is visible to every node and is not in the mask.
+ *   sel_parent as written by prune_topB (parents precede children).
+ */
+int build_tree_mask(const int32_t* sel_parent, const int32_t* n_sel, int R, int B,
+                    uint32_t* mask, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Verification: one tree-attention layer                                    */
+/* ------------------------------------------------------------------------ */
+
+size_t tree_attention_workspace_size(int n_tree, int P, int Hq, int Hkv, int hd);
+
+/*
+ * tree_attention_verify - one attention layer of the target's single
+ * verification forward over the tree ([P1] Core Mechanism, last step; [P2]
+ * part 2, Verificatie; [P3]).  Query i (a tree node) of head h attends to all
+ * P prefix keys and to the tree keys its mask row marks; key/value head
+ * h / (Hq / Hkv) (grouped-query attention).  Softmax in fp32.
+ *   q        [n_tree][Hq][hd]  bf16
+ *   k_prefix, v_prefix [P][Hkv][hd] bf16
+ *   k_tree,   v_tree   [n_tree][Hkv][hd] bf16
+ *   mask     [n_tree][ceil(n_tree/32)] u32 (build_tree_mask row layout)
+ *   out      [n_tree][Hq][hd]  f32
+ *   hd == 128, Hq % Hkv == 0, 1 <= n_tree <= 1024, P >= 0.
+ */
+int tree_attention_verify(const void* q, const void* k_prefix, const void* v_prefix,
+                          const void* k_tree, const void* v_tree, const uint32_t* mask,
+                          int n_tree, int P, int Hq, int Hkv, int hd, float scale,
+                          float* out, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Kernel timing (off by default)                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Kernel classes that can be timed. */
+typedef enum {
+  DT_K_GEMM1 = 0,   /* state update, first projection (+ GELU)      */
+  DT_K_GEMM2 = 1,   /* state update, second projection (+ residual)  */
+  DT_K_HEAD = 2,    /* corrected-logit head + per-tile softmax/top-k */
+  DT_K_MERGE = 3,   /* per-row merge + beam select                   */
+  DT_K_COUNT = 4
+} dt_kernel_class;
+
+/*
+ * dartree_timing_enable - when enabled, every launch of a kernel class is
+ * bracketed by HIP events recorded on the launch's stream; after the caller
+ * synchronises, dartree_timing_read returns the summed milliseconds and the
+ * launch count since the last reset.  Process-wide; not thread-safe; adds an
+ * event pair per launch.
+ */
+int dartree_timing_enable(int enable);
+int dartree_timing_reset(void);
+int dartree_timing_read(int kernel_class, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DARTREE_H */

@@ -1,0 +1,2 @@
+"""fp64 CPU oracle (test infrastructure only; never used by the product path)."""
+from . import dartree_oracle  # noqa: F401

@@ -1,0 +1,329 @@
+"""fp64 CPU oracle for DARTree's depth-wise batched draft-supertree construction.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import or call this module.  It
+shares no code with the HIP library and never imports it.
+
+Sources (page title, section):
+
+* "DARTree: Teaching a Chain-Trained Corrector to Think in Trees" (alanhou.org),
+  section "Core Mechanism" and its diagram: at each depth one batched call of
+  the AR correction head over all W surviving paths, top-k children per path,
+  candidates scored by accumulated path probability, keep the top W, repeat for
+  D depths (D head calls); then best-first pruning over the cached scores
+  builds the verification tree and its sparse attention mask.
+* "Technische Samenvatting: DARTree" (gist.science), section "Methodologie",
+  part 1 "Depth-Wise Parallel AR Expansie": candidates scored by corrected
+  cumulative probability, the top-W branches kept and their correction states
+  carried forward; part 2 "Deferred Best-First Pruning": one global top-B over
+  all materialised prefixes, equal (Lemma 1) to the sequential best-first
+  max-heap selection when the depth bonus beta is <= 0.
+* "Accelerating Language Models with Diffusion Draft Trees" (legiblepapers),
+  "Summary & Methodology Analysis": global top-W child prefixes per depth (W the
+  layer width), global top-B nodes (B the verification budget), prefix tree
+  verified with a tree-attention mask in one forward.
+
+The pages give no head architecture.  The synthetic correction head used here
+is the workload recipe: ``s' = s + GELU((E[tok] + h_t) W1) W2`` with the exact
+erf GELU, logits ``z = s' U``, temperature log-softmax ``z/T - logsumexp(z/T)``.
+
+Readings where the pages are silent (each listed in the design notes):
+
+* the root (last verified token) is a single frontier row at depth 0, expanded
+  like any node, so the width at depth t is ``min(W, n_{t-1} * k)``;
+* h_t feeds the step that produces the depth-t tokens; the carried state of a
+  kept child is its parent's updated state, and the child's token is consumed
+  by the next depth's update;
+* T = 0 is the T -> 0+ limit: only the lowest-index argmax has finite
+  log-probability (0), so each row has one child;
+* tie-breaks: children by (logp desc, token asc); survivors by (score desc,
+  parent slot asc, child rank asc); pruning by (prio desc, depth asc,
+  slot asc) with ``prio = score + beta * depth``;
+* the verification tree is emitted in (depth, slot) order; its mask row i holds
+  node i and its ancestors among the draft nodes (the prefix is always visible
+  and is not part of the bitmask).
+"""
+from __future__ import annotations
+
+import heapq
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+from scipy.special import erf
+
+NEG_INF = -math.inf
+
+
+# ----------------------------------------------------------------------------
+# weights
+# ----------------------------------------------------------------------------
+def _widen(a: np.ndarray, wdtype: str) -> np.ndarray:
+    """Storage array -> exact float64 (bf16 bit patterns or float32)."""
+    if wdtype == "bf16":
+        return (np.asarray(a, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(a, np.float32).astype(np.float64)
+
+
+class OracleHead:
+    """The synthetic correction head in math layout, fp64.
+
+    Takes storage-layout arrays: E [V][d], W1t [4d][d], W2t [d][4d], Ut [V][d]
+    (float32 or bf16 bit patterns).  W1 = W1t^T, W2 = W2t^T, U = Ut^T.
+    The output head U is widened lazily in column chunks unless ``cache_u``.
+    """
+
+    def __init__(self, wdtype, E, W1t, W2t, Ut, cache_u=True, chunk=16384):
+        self.wdtype = wdtype
+        self.V, self.d = Ut.shape
+        self._E = E
+        self.W1 = _widen(W1t, wdtype).T          # [d][4d]
+        self.W2 = _widen(W2t, wdtype).T          # [4d][d]
+        self._Ut = Ut
+        self.chunk = chunk
+        self._U = _widen(Ut, wdtype).T if cache_u else None   # [d][V]
+
+    def embed(self, tok) -> np.ndarray:
+        return _widen(self._E[np.asarray(tok, np.int64)], self.wdtype)
+
+    def logits(self, s: np.ndarray) -> np.ndarray:
+        """z = s U for rows s [n][d] -> [n][V] fp64."""
+        if self._U is not None:
+            return s @ self._U
+        z = np.empty((s.shape[0], self.V), np.float64)
+        for lo in range(0, self.V, self.chunk):
+            hi = min(self.V, lo + self.chunk)
+            z[:, lo:hi] = s @ _widen(self._Ut[lo:hi], self.wdtype).T
+        return z
+
+
+# ----------------------------------------------------------------------------
+# one correction-head step (workload recipe)
+# ----------------------------------------------------------------------------
+def gelu(x: np.ndarray) -> np.ndarray:
+    """Exact GELU, x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2))."""
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+def state_update(head: OracleHead, s: np.ndarray, tok, h_t: np.ndarray) -> np.ndarray:
+    """s' = s + GELU((E[tok] + h_t) W1) W2 for every frontier row (fp64)."""
+    x = head.embed(tok) + np.asarray(h_t, np.float64)[None, :]
+    return np.asarray(s, np.float64) + gelu(x @ head.W1) @ head.W2
+
+
+def log_softmax_T(z: np.ndarray, T: float) -> np.ndarray:
+    """Temperature log-softmax of one row, fp64, max-shifted.
+
+    T > 0: z/T - log sum exp(z/T).  T == 0: the T -> 0+ limit, 0 at the
+    lowest-index maximum of z and -inf elsewhere.
+    """
+    z = np.asarray(z, np.float64)
+    if T == 0.0:
+        out = np.full(z.shape, NEG_INF)
+        out[int(np.argmax(z))] = 0.0        # argmax returns the first maximum
+        return out
+    y = z / T
+    m = np.max(y)
+    return y - (m + math.log(np.sum(np.exp(y - m))))
+
+
+def topk_children(logp: np.ndarray, k: int):
+    """The k best tokens of one row by (logp desc, token asc), finite only.
+
+    Returns (tokens int64 [<=k], logps float64 [<=k]).
+    """
+    idx = np.arange(logp.size)
+    order = np.lexsort((idx, -logp))          # primary -logp, then token
+    order = order[np.isfinite(logp[order])][:k]
+    return order.astype(np.int64), logp[order]
+
+
+def entropy_T(z: np.ndarray, T: float) -> float:
+    """Entropy (nats) of softmax(z / T); used only for input calibration."""
+    lp = log_softmax_T(z, T)
+    p = np.exp(lp)
+    return float(-np.sum(p[p > 0] * lp[p > 0]))
+
+
+# ----------------------------------------------------------------------------
+# depth-wise batched supertree construction
+# ----------------------------------------------------------------------------
+@dataclass
+class Supertree:
+    """Scored pool of one request: slot j at depth t (0-based t = depth - 1)."""
+    tok: np.ndarray          # [D][W] int64, -1 where invalid
+    parent: np.ndarray       # [D][W] int64, parent slot at depth t-1 (-1 at t=0 / invalid)
+    score: np.ndarray        # [D][W] float64, accumulated log-prob, -inf where invalid
+    n_valid: np.ndarray      # [D] int64
+    head_calls: int = 0
+    entropies: list = field(default_factory=list)   # per depth: entropies of the rows (T>0)
+    lse: list = field(default_factory=list)         # per depth: logsumexp(z/T) of each row
+
+
+def build_supertree(head: OracleHead, h: np.ndarray, s0: np.ndarray, root_tok: int,
+                    D: int, W: int, k: int, T: float,
+                    want_entropy: bool = False) -> Supertree:
+    """Depth-wise batched construction for one request (fp64)."""
+    pool_tok = np.full((D, W), -1, np.int64)
+    pool_parent = np.full((D, W), -1, np.int64)
+    pool_score = np.full((D, W), NEG_INF)
+    n_valid = np.zeros(D, np.int64)
+    out = Supertree(pool_tok, pool_parent, pool_score, n_valid)
+
+    f_state = np.asarray(s0, np.float64)[None, :]     # frontier: root only
+    f_tok = np.array([root_tok], np.int64)
+    f_score = np.array([0.0])
+    for t in range(D):
+        # one batched head call over every frontier row
+        out.head_calls += 1
+        s_new = state_update(head, f_state, f_tok, h[t])
+        z = head.logits(s_new)
+        cands = []                                    # (score, parent, rank, token)
+        ents, lses = [], []
+        for i in range(z.shape[0]):
+            lp = log_softmax_T(z[i], T)
+            if T > 0.0:
+                y = z[i] / T
+                lses.append(float(np.max(y) + math.log(np.sum(np.exp(y - np.max(y))))))
+                if want_entropy:
+                    ents.append(entropy_T(z[i], T))
+            toks, lps = topk_children(lp, k)
+            for r in range(toks.size):
+                cands.append((f_score[i] + lps[r], i, r, int(toks[r])))
+        out.entropies.append(ents)
+        out.lse.append(lses)
+        cands.sort(key=lambda c: (-c[0], c[1], c[2]))
+        keep = cands[:W]
+        n = len(keep)
+        n_valid[t] = n
+        for j, (sc, i, r, c) in enumerate(keep):
+            pool_tok[t, j] = c
+            pool_parent[t, j] = i if t > 0 else -1
+            pool_score[t, j] = sc
+        # carry the parent's updated state; the child's token is consumed next
+        f_state = s_new[[c[1] for c in keep]]
+        f_tok = np.array([c[3] for c in keep], np.int64)
+        f_score = np.array([c[0] for c in keep])
+    return out
+
+
+# ----------------------------------------------------------------------------
+# deferred best-first pruning
+# ----------------------------------------------------------------------------
+@dataclass
+class VerifyTree:
+    node: np.ndarray         # [n] flat pool index t*W + j
+    parent: np.ndarray       # [n] index into this list, -1 for depth-1 nodes
+    depth: np.ndarray        # [n] 1-based depth
+    n: int
+
+
+def _pool_nodes(score, n_valid):
+    return [(t, j) for t in range(score.shape[0]) for j in range(int(n_valid[t]))]
+
+
+def prune_topB(score, parent, n_valid, B: int, beta: float) -> VerifyTree:
+    """Global top-B over the scored pool with prio = score + beta * depth.
+
+    Order (prio desc, depth asc, slot asc); the chosen nodes are emitted in
+    (depth, slot) order with parents remapped to emitted indices.
+    """
+    D, W = score.shape
+    nodes = _pool_nodes(score, n_valid)
+    prio = {n: float(score[n]) + beta * (n[0] + 1) for n in nodes}
+    ranked = sorted(nodes, key=lambda n: (-prio[n], n[0], n[1]))
+    chosen = sorted(ranked[:min(B, len(nodes))])
+    index = {n: i for i, n in enumerate(chosen)}
+    m = len(chosen)
+    node = np.array([t * W + j for t, j in chosen], np.int64)
+    depth = np.array([t + 1 for t, _ in chosen], np.int64)
+    par = np.full(m, -1, np.int64)
+    for i, (t, j) in enumerate(chosen):
+        if t > 0:
+            p = (t - 1, int(parent[t, j]))
+            if p not in index:
+                raise AssertionError(f"selection not ancestor-closed at {(t, j)}")
+            par[i] = index[p]
+    return VerifyTree(node, par, depth, m)
+
+
+def heap_prune(score, parent, n_valid, B: int, beta: float) -> set:
+    """Sequential best-first selection with a max-heap over the cached pool.
+
+    Start from the depth-1 nodes; pop the best (prio desc, depth asc, slot
+    asc), then push its children; stop after B pops.  Returns the popped set of
+    (t, j).  (Lemma 1 states this equals the global top-B when beta <= 0.)
+    """
+    D, W = score.shape
+    kids = {}
+    for t in range(1, D):
+        for j in range(int(n_valid[t])):
+            kids.setdefault((t - 1, int(parent[t, j])), []).append((t, j))
+
+    def key(n):
+        return (-(float(score[n]) + beta * (n[0] + 1)), n[0], n[1])
+
+    heap = [key((0, j)) for j in range(int(n_valid[0]))]
+    heapq.heapify(heap)
+    popped = set()
+    while heap and len(popped) < B:
+        _, t, j = heapq.heappop(heap)
+        popped.add((t, j))
+        for c in kids.get((t, j), []):
+            heapq.heappush(heap, key(c))
+    return popped
+
+
+# ----------------------------------------------------------------------------
+# ancestor mask
+# ----------------------------------------------------------------------------
+def tree_mask(parent: np.ndarray, n: int, B: int) -> np.ndarray:
+    """Bitmask [B][ceil(B/32)] uint32: row i has bit i and the bits of all its
+    ancestors among the tree nodes (bit b of word w is node 32 w + b)."""
+    words = (B + 31) // 32
+    mask = np.zeros((B, words), np.uint32)
+    for i in range(n):
+        a = i
+        while a >= 0:
+            mask[i, a // 32] |= np.uint32(1 << (a % 32))
+            a = int(parent[a])
+    return mask
+
+
+def mask_to_bool(mask: np.ndarray, n: int) -> np.ndarray:
+    """Visible[i][j] (j a tree node) from the bitmask."""
+    vis = np.zeros((n, n), bool)
+    for i in range(n):
+        for j in range(n):
+            vis[i, j] = bool((int(mask[i, j // 32]) >> (j % 32)) & 1)
+    return vis
+
+
+# ----------------------------------------------------------------------------
+# verification: one tree-attention layer
+# ----------------------------------------------------------------------------
+def tree_attention(q, k_prefix, v_prefix, k_tree, v_tree, mask, n: int, scale: float):
+    """Tree attention in fp64.
+
+    q [n][Hq][hd]; k/v_prefix [P][Hkv][hd]; k/v_tree [n][Hkv][hd]; query head h
+    reads key/value head h // (Hq / Hkv).  Each tree query sees every prefix key
+    and the tree keys its mask row marks.  Returns out [n][Hq][hd] fp64.
+    """
+    q = np.asarray(q, np.float64)
+    kp, vp = np.asarray(k_prefix, np.float64), np.asarray(v_prefix, np.float64)
+    kt, vt = np.asarray(k_tree, np.float64), np.asarray(v_tree, np.float64)
+    Hq, Hkv = q.shape[1], kp.shape[1]
+    group = Hq // Hkv
+    vis = mask_to_bool(mask, n)
+    out = np.zeros((n, Hq, q.shape[2]))
+    for h in range(Hq):
+        g = h // group
+        sp = (q[:n, h] @ kp[:, g].T) * scale                 # [n][P]
+        st = (q[:n, h] @ kt[:n, g].T) * scale                # [n][n]
+        st = np.where(vis, st, NEG_INF)
+        s = np.concatenate([sp, st], axis=1)
+        m = np.max(s, axis=1, keepdims=True)
+        p = np.exp(s - m)
+        p /= np.sum(p, axis=1, keepdims=True)
+        out[:, h] = p @ np.concatenate([vp[:, g], vt[:n, g]], axis=0)
+    return out

@@ -1,0 +1,419 @@
+"""Pins of the fp64 oracle to facts outside itself.
+
+Each test checks the oracle against a closed form, a textbook special case, a
+library routine it does not use, brute force on tiny inputs, or a hand-worked
+example under tests/golden/.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+from hypothesis import given, settings, strategies as st
+
+from oracle import dartree_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+
+
+def gold():
+    with open(GOLD) as f:
+        return json.load(f)
+
+
+def tiny_head(V=7, d=8, seed=0, wscale=0.5, uscale=1.5):
+    """A float32 head small enough for brute force (storage layout)."""
+    g = np.random.default_rng(seed)
+    E = (g.standard_normal((V, d)) * wscale).astype(np.float32)
+    W1t = (g.standard_normal((4 * d, d)) * wscale).astype(np.float32)
+    W2t = (g.standard_normal((d, 4 * d)) * wscale).astype(np.float32)
+    Ut = (g.standard_normal((V, d)) * uscale).astype(np.float32)
+    return O.OracleHead("f32", E, W1t, W2t, Ut)
+
+
+# ----------------------------------------------------------------------------
+# GELU and the state update
+# ----------------------------------------------------------------------------
+def test_gelu_matches_math_erf_and_table_values():
+    xs = np.linspace(-8, 8, 1601)
+    ref = np.array([0.5 * x * (1 + math.erf(x / math.sqrt(2))) for x in xs])
+    assert np.max(np.abs(O.gelu(xs) - ref)) < 1e-15
+    # textbook Phi values: GELU(1) = Phi(1), GELU(2) = 2 Phi(2)
+    assert abs(O.gelu(np.array(1.0)) - 0.8413447460685429) < 1e-15
+    assert abs(O.gelu(np.array(2.0)) - 2 * 0.9772498680518208) < 1e-15
+    # GELU(x) - GELU(-x) = x, GELU(0) = 0, GELU -> identity / 0 in the tails
+    assert np.max(np.abs(O.gelu(xs) - O.gelu(-xs) - xs)) < 1e-14
+    assert O.gelu(np.array(0.0)) == 0.0
+    assert abs(O.gelu(np.array(40.0)) - 40.0) < 1e-12
+    assert abs(O.gelu(np.array(-40.0))) < 1e-12
+
+
+def test_state_update_hand_example():
+    g = gold()["state_update_d1"]
+    E = np.array(g["E"], np.float32)
+    W1t = np.array(g["W1"], np.float32).T.copy()      # stored transposed
+    W2t = np.array(g["W2"], np.float32).T.copy()
+    head = O.OracleHead("f32", E, W1t, W2t, np.zeros((2, 1), np.float32))
+    s = O.state_update(head, np.array([g["s"]]), [g["tok"]], np.array(g["h"]))
+    assert abs(s[0, 0] - g["s_new"][0]) < 1e-14
+
+
+def test_state_update_degenerate_weights_keep_state():
+    head = tiny_head()
+    s = np.random.default_rng(1).standard_normal((3, 8))
+    h = np.random.default_rng(2).standard_normal(8)
+    for zero in ("W1", "W2"):
+        hz = tiny_head()
+        setattr(hz, zero, np.zeros_like(getattr(hz, zero)))
+        assert np.array_equal(O.state_update(hz, s, [0, 1, 2], h), s)
+    # E[tok] + h = 0 -> GELU(0) = 0 -> state unchanged
+    hz = tiny_head()
+    tok = [4, 4, 4]
+    s2 = O.state_update(hz, s, tok, -hz.embed([4])[0])
+    assert np.array_equal(s2, s)
+    assert head.d == 8
+
+
+def test_state_update_linear_regime_orientation():
+    # With a large positive pre-activation GELU is the identity, so the update
+    # is the linear map s + x W1 W2, computed here by a different association.
+    d = 5
+    g = np.random.default_rng(3)
+    E = np.zeros((3, d), np.float32)
+    W1 = np.abs(g.standard_normal((d, 4 * d))).astype(np.float32) + 1.0
+    W2 = g.standard_normal((4 * d, d)).astype(np.float32)
+    head = O.OracleHead("f32", E, W1.T.copy(), W2.T.copy(), np.zeros((3, d), np.float32))
+    x = np.full(d, 20.0)
+    s = g.standard_normal((1, d))
+    got = O.state_update(head, s, [1], x)
+    want = s + x[None, :] @ (W1.astype(np.float64) @ W2.astype(np.float64))
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-9)
+
+
+def test_head_storage_layout_is_transposed_u():
+    V, d = 6, 4
+    Ut = np.zeros((V, d), np.float32)
+    Ut[3, 1] = 1.0
+    head = O.OracleHead("f32", np.zeros((V, d), np.float32), np.zeros((4 * d, d), np.float32),
+                        np.zeros((d, 4 * d), np.float32), Ut)
+    s = np.array([[0.1, 0.7, -0.2, 0.3]])
+    z = head.logits(s)
+    assert z[0, 3] == pytest.approx(0.7) and np.count_nonzero(z) == 1
+
+
+def test_bf16_widening_is_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0001, 0x7F7F], np.uint16)
+    want = [1.0, -1.0, 3.140625, 2.0 ** -133, 3.3895313892515355e38]
+    head = O.OracleHead("bf16", bits.reshape(5, 1), np.zeros((4, 1), np.uint16),
+                        np.zeros((1, 4), np.uint16), np.zeros((5, 1), np.uint16))
+    got = head.embed(np.arange(5))[:, 0]
+    assert list(got) == want
+
+
+def test_chunked_and_cached_logits_agree():
+    g = np.random.default_rng(5)
+    V, d = 1000, 16
+    Ut = g.standard_normal((V, d)).astype(np.float32)
+    args = ("f32", np.zeros((V, d), np.float32), np.zeros((4 * d, d), np.float32),
+            np.zeros((d, 4 * d), np.float32), Ut)
+    a = O.OracleHead(*args, cache_u=True)
+    b = O.OracleHead(*args, cache_u=False, chunk=96)
+    s = g.standard_normal((3, d))
+    assert np.allclose(a.logits(s), b.logits(s), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# temperature log-softmax and top-k
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [0.25, 1.0, 3.0])
+def test_log_softmax_matches_scipy(T):
+    g = np.random.default_rng(7)
+    for scale in (1.0, 30.0, 300.0):
+        z = g.standard_normal(5000) * scale
+        got = O.log_softmax_T(z, T)
+        want = scipy.special.log_softmax(z / T)
+        assert np.max(np.abs(got - want)) < 1e-9 * max(1.0, scale / T)
+        assert abs(np.sum(np.exp(got)) - 1.0) < 1e-12
+
+
+def test_log_softmax_T0_is_lowest_index_argmax():
+    z = np.array([1.0, 3.0, -2.0, 3.0, 0.5])
+    lp = O.log_softmax_T(z, 0.0)
+    assert lp[1] == 0.0 and np.all(np.isneginf(np.delete(lp, 1)))
+    # the T -> 0+ limit of the temperature log-softmax on a gap-ful row
+    z2 = np.array([0.0, 1.0, 0.2])
+    lim = scipy.special.log_softmax(z2 / 1e-4)
+    assert np.argmax(lim) == 1 and abs(lim[1]) < 1e-12 and lim[0] < -1e3
+
+
+@given(st.lists(st.integers(-3, 3), min_size=1, max_size=12), st.integers(1, 14))
+@settings(max_examples=200, deadline=None)
+def test_topk_children_brute_force(vals, k):
+    lp = np.array(vals, np.float64)
+    toks, lps = O.topk_children(lp, k)
+    m = min(k, lp.size)
+    assert toks.size == m
+    chosen = set(toks.tolist())
+    # every chosen >= every unchosen, equal values resolved to the lower token
+    for a in chosen:
+        for b in set(range(lp.size)) - chosen:
+            assert lp[a] > lp[b] or (lp[a] == lp[b] and a < b)
+    # sorted by (logp desc, token asc)
+    keys = [(-lp[t], t) for t in toks]
+    assert keys == sorted(keys)
+    assert np.array_equal(lps, lp[toks])
+
+
+def test_topk_children_skips_minus_inf():
+    lp = np.array([-np.inf, -1.0, -np.inf, -0.5])
+    toks, _ = O.topk_children(lp, 4)
+    assert toks.tolist() == [3, 1]
+
+
+# ----------------------------------------------------------------------------
+# depth-wise batched construction
+# ----------------------------------------------------------------------------
+def _greedy_chain(head, h, s0, root, D):
+    """Textbook greedy decoding: feed back the argmax token each step."""
+    s, tok, score, toks, scores = np.asarray(s0, np.float64)[None], root, 0.0, [], []
+    for t in range(D):
+        s = O.state_update(head, s, [tok], h[t])
+        lp = scipy.special.log_softmax(head.logits(s)[0])
+        tok = int(np.argmax(lp))
+        score += lp[tok]
+        toks.append(tok); scores.append(score)
+    return toks, scores
+
+
+def _inputs(head, D, seed=11):
+    g = np.random.default_rng(seed)
+    return g.standard_normal((D, head.d)), g.standard_normal(head.d)
+
+
+def test_width_one_is_the_greedy_chain():
+    head = tiny_head(V=40, d=8)
+    h, s0 = _inputs(head, 6)
+    tree = O.build_supertree(head, h, s0, 3, D=6, W=1, k=4, T=1.0)
+    toks, scores = _greedy_chain(head, h, s0, 3, 6)
+    assert tree.tok[:, 0].tolist() == toks
+    assert np.allclose(tree.score[:, 0], scores, atol=1e-12)
+    assert tree.n_valid.tolist() == [1] * 6
+
+
+def test_T0_is_the_same_chain_with_zero_scores():
+    head = tiny_head(V=40, d=8)
+    h, s0 = _inputs(head, 6)
+    t0 = O.build_supertree(head, h, s0, 3, D=6, W=5, k=4, T=0.0)
+    toks, _ = _greedy_chain(head, h, s0, 3, 6)
+    assert t0.n_valid.tolist() == [1] * 6
+    assert t0.tok[:, 0].tolist() == toks
+    assert np.all(t0.score[:, 0] == 0.0)
+    assert np.all(t0.tok[:, 1:] == -1)
+
+
+def test_exhaustive_enumeration_when_beam_keeps_everything():
+    V, D = 3, 3
+    head = tiny_head(V=V, d=6, seed=4)
+    h, s0 = _inputs(head, D, seed=12)
+    tree = O.build_supertree(head, h, s0, 0, D=D, W=V ** D, k=V, T=1.0)
+    # brute force: every token sequence, its state chain and summed log-prob
+    for t in range(1, D + 1):
+        want = {}
+        for seq in itertools.product(range(V), repeat=t):
+            s, tok, sc = np.asarray(s0)[None], 0, 0.0
+            for i, c in enumerate(seq):
+                s = O.state_update(head, s, [tok], h[i])
+                sc += scipy.special.log_softmax(head.logits(s)[0])[c]
+                tok = c
+            want[seq] = sc
+        assert int(tree.n_valid[t - 1]) == V ** t
+        got = {}
+        for j in range(V ** t):
+            seq, tt, jj = [], t - 1, j
+            while tt >= 0:
+                seq.append(int(tree.tok[tt, jj]))
+                jj = int(tree.parent[tt, jj]); tt -= 1
+            got[tuple(reversed(seq))] = tree.score[t - 1, j]
+        assert got.keys() == want.keys()
+        assert max(abs(got[s] - want[s]) for s in want) < 1e-12
+        # the depth-t path probabilities form a distribution
+        assert abs(sum(math.exp(v) for v in got.values()) - 1.0) < 1e-12
+        # slots in non-increasing score order
+        assert np.all(np.diff(tree.score[t - 1, :V ** t]) <= 0)
+
+
+def test_width_formula_head_calls_and_structure():
+    head = tiny_head(V=50, d=8)
+    h, s0 = _inputs(head, 7)
+    for W, k in ((4, 4), (16, 3), (5, 8), (1, 1)):
+        tree = O.build_supertree(head, h, s0, 2, D=7, W=W, k=k, T=1.0)
+        assert tree.head_calls == 7
+        n = 1
+        for t in range(7):
+            n = min(W, n * k)
+            assert tree.n_valid[t] == n
+            for j in range(n):
+                p = tree.parent[t, j]
+                if t == 0:
+                    assert p == -1 and tree.score[t, j] <= 0
+                else:
+                    assert 0 <= p < tree.n_valid[t - 1]
+                    assert tree.score[t, j] <= tree.score[t - 1, p]
+            assert np.all(np.isneginf(tree.score[t, n:]))
+
+
+def test_survivor_tie_break_on_exact_ties():
+    # With E = 0 and h = 0 the update leaves every state equal to s0, so every
+    # row has the same children a, b, c with log-probs l0 > l1 > l2.  At depth
+    # 2 the candidates (parent 0, b) and (parent 1, a) both score l0 + l1
+    # exactly; the tie goes to the lower parent slot.
+    V, d = 9, 4
+    Ut = np.random.default_rng(0).standard_normal((V, d)).astype(np.float32)
+    head = O.OracleHead("f32", np.zeros((V, d), np.float32), np.zeros((4 * d, d), np.float32),
+                        np.zeros((d, 4 * d), np.float32), Ut)
+    s0 = np.ones(d)
+    tree = O.build_supertree(head, np.zeros((2, d)), s0, 0, D=2, W=6, k=3, T=1.0)
+    assert tree.n_valid.tolist() == [3, 6]
+    a, b, c = tree.tok[0, :3].tolist()
+    got = [(int(tree.parent[1, j]), int(tree.tok[1, j])) for j in range(3)]
+    assert got == [(0, a), (0, b), (1, a)]
+    assert tree.score[1, 1] == tree.score[1, 2]
+
+
+# ----------------------------------------------------------------------------
+# deferred pruning (Lemma 1), ancestor closure, mask
+# ----------------------------------------------------------------------------
+def test_prune_and_mask_hand_examples():
+    g = gold()["pool_prune_mask"]
+    score = np.array(g["score"]); parent = np.array(g["parent"]); nv = np.array(g["n_valid"])
+    for case in g["cases"]:
+        vt = O.prune_topB(score, parent, nv, case["B"], case["beta"])
+        assert vt.node.tolist() == case["node"]
+        assert vt.parent.tolist() == case["sel_parent"]
+        assert vt.depth.tolist() == case["depth"]
+        B = case["B"]
+        m = O.tree_mask(vt.parent, vt.n, B)
+        assert m[:vt.n, 0].tolist() == case["mask"]
+        assert np.all(m[vt.n:] == 0)
+
+
+@st.composite
+def pools(draw):
+    D = draw(st.integers(1, 4))
+    W = draw(st.integers(1, 4))
+    integer = draw(st.booleans())
+    score = np.full((D, W), -np.inf)
+    parent = np.full((D, W), -1, np.int64)
+    nv = np.zeros(D, np.int64)
+    prev = 1
+    for t in range(D):
+        n = draw(st.integers(1, W)) if prev > 0 else 0
+        nv[t] = n
+        for j in range(n):
+            p = draw(st.integers(0, prev - 1)) if t > 0 else -1
+            base = 0.0 if t == 0 else score[t - 1, p]
+            step = draw(st.integers(0, 3)) if integer else draw(
+                st.floats(0, 3, allow_nan=False, allow_infinity=False))
+            score[t, j] = base - step
+            parent[t, j] = p
+        prev = n
+    return score, parent, nv
+
+
+@given(pools(), st.integers(1, 20), st.sampled_from([0.0, -0.5, -1.0, -2.0]))
+@settings(max_examples=400, deadline=None)
+def test_lemma1_top_b_equals_best_first_heap(pool, B, beta):
+    score, parent, nv = pool
+    vt = O.prune_topB(score, parent, nv, B, beta)
+    W = score.shape[1]
+    got = {divmod(int(x), W) for x in vt.node}
+    assert got == O.heap_prune(score, parent, nv, B, beta)
+    assert vt.n == min(B, int(nv.sum()))
+    # ancestor closed, emitted in (depth, slot) order, parents index earlier rows
+    for i in range(vt.n):
+        assert vt.parent[i] < i
+        assert (vt.parent[i] == -1) == (vt.depth[i] == 1)
+    assert list(vt.node) == sorted(vt.node)
+
+
+def test_lemma1_needs_nonpositive_beta():
+    # a deep node with a higher priority than a shallow one once beta > 0:
+    # global top-B then picks a node whose parent it does not pick
+    score = np.array([[-1.0, -1.05], [-1.1, -np.inf]])
+    parent = np.array([[-1, -1], [1, -1]])
+    nv = np.array([2, 1])
+    beta = 1.0     # prios: (0,0) 0.0, (0,1) -0.05, (1,0) 0.9
+    with pytest.raises(AssertionError):
+        O.prune_topB(score, parent, nv, 1, beta)
+    assert O.heap_prune(score, parent, nv, 1, beta) == {(0, 0)}
+
+
+def test_mask_closed_forms():
+    B = 70
+    chain = np.arange(-1, B - 1)
+    m = O.tree_mask(chain, B, B)
+    vis = O.mask_to_bool(m, B)
+    assert np.array_equal(vis, np.tril(np.ones((B, B), bool)))
+    star = np.full(B, -1)
+    assert np.array_equal(O.mask_to_bool(O.tree_mask(star, B, B), B), np.eye(B, dtype=bool))
+    # popcount of a row = depth of the node
+    g = np.random.default_rng(0)
+    par = np.array([-1] + [int(g.integers(-1, i)) for i in range(1, B)])
+    m = O.tree_mask(par, B, B)
+    for i in range(B):
+        dep, a = 0, i
+        while a >= 0:
+            dep += 1; a = par[a]
+        assert sum(bin(int(w)).count("1") for w in m[i]) == dep
+
+
+# ----------------------------------------------------------------------------
+# tree attention
+# ----------------------------------------------------------------------------
+def _attn_inputs(n, P, Hq, Hkv, hd, seed=0):
+    g = np.random.default_rng(seed)
+    return (g.standard_normal((n, Hq, hd)), g.standard_normal((P, Hkv, hd)),
+            g.standard_normal((P, Hkv, hd)), g.standard_normal((n, Hkv, hd)),
+            g.standard_normal((n, Hkv, hd)))
+
+
+def test_attention_star_tree_without_prefix_returns_own_value():
+    n, Hq, Hkv, hd = 9, 4, 2, 8
+    q, kp, vp, kt, vt = _attn_inputs(n, 0, Hq, Hkv, hd)
+    m = O.tree_mask(np.full(n, -1), n, n)
+    out = O.tree_attention(q, kp, vp, kt, vt, m, n, 0.3)
+    for h in range(Hq):
+        assert np.array_equal(out[:, h], vt[:, h // 2])
+
+
+def test_attention_chain_is_causal_sdpa():
+    n, P, Hq, Hkv, hd = 12, 0, 4, 4, 16
+    q, kp, vp, kt, vt = _attn_inputs(n, P, Hq, Hkv, hd, seed=1)
+    m = O.tree_mask(np.arange(-1, n - 1), n, n)
+    out = O.tree_attention(q, kp, vp, kt, vt, m, n, 1 / 4)
+    tq = torch.from_numpy(q).permute(1, 0, 2)
+    tk = torch.from_numpy(kt).permute(1, 0, 2)
+    tv = torch.from_numpy(vt).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=1 / 4)
+    assert np.max(np.abs(out - ref.permute(1, 0, 2).numpy())) < 1e-12
+
+
+def test_attention_prefix_and_tree_mask_match_sdpa_with_gqa():
+    n, P, Hq, Hkv, hd = 10, 37, 8, 2, 16
+    q, kp, vp, kt, vt = _attn_inputs(n, P, Hq, Hkv, hd, seed=2)
+    g = np.random.default_rng(3)
+    par = np.array([-1] + [int(g.integers(-1, i)) for i in range(1, n)])
+    m = O.tree_mask(par, n, n)
+    out = O.tree_attention(q, kp, vp, kt, vt, m, n, 0.17)
+    vis = torch.from_numpy(np.concatenate([np.ones((n, P), bool), O.mask_to_bool(m, n)], 1))
+    K = torch.from_numpy(np.concatenate([kp, kt], 0)).permute(1, 0, 2)
+    Vv = torch.from_numpy(np.concatenate([vp, vt], 0)).permute(1, 0, 2)
+    K = K.repeat_interleave(Hq // Hkv, 0)
+    Vv = Vv.repeat_interleave(Hq // Hkv, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2), K, Vv, attn_mask=vis, scale=0.17)
+    assert np.max(np.abs(out - ref.permute(1, 0, 2).numpy())) < 1e-12
