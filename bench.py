@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Throughput of DARTree draft-supertree construction on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input,
+with every input already resident in HBM:
+  build_supertree (D depths of state update, corrected-logit head, fused
+  log-softmax/top-k, beam select) -> prune_topB -> build_tree_mask ->
+  tree_attention_verify (one verification layer over the pruned tree).
+
+Prints one JSON line.  `value` is supertree builds per second (R per step).
+The roofline object reports the corrected-logit head kernel: algorithmic
+bytes per launch (2 d V, the bf16 output head streamed once) divided by its
+average launch time measured with HIP events on the launch stream.
+The cpu_baseline object times the fp64 oracle on a bounded sample.
+
+  python bench.py [--steps K] [--warmup W] [--workload qwen3_4b]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "supertree builds/s (D,W,k,V) + achieved HBM GB/s vs peak; oracle-exact"
+HBM_PEAK_GBS = 8000.0
+VERIFY = dict(Hq=32, Hkv=8, hd=128, P=4096)   # Qwen3-4B/8B attention layer shape
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_4b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-builds", type=int, default=1,
+                    help="oracle builds timed for cpu_baseline")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the method's "
+              "hot path runs on a single device, see the design notes on sharding.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from draft_tree_construction_02_amd import _abi as A
+    from draft_tree_construction_02_amd import synth
+
+    wl = synth.workloads()[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    hw, req = synth.make_workload_inputs(wl)
+    log(f"[bench] inputs for {wl.name} drawn in {time.time() - t0:.1f}s")
+
+    def up16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def up(a):
+        return up16(a) if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    head = A.Head(up(hw.E), up(hw.W1t), up(hw.W2t), up(hw.Ut))
+    h, s0, root = (torch.from_numpy(req.h).to(dev), torch.from_numpy(req.s0).to(dev),
+                   torch.from_numpy(req.root_tok).to(dev))
+    R, D, W, k, B = wl.R, wl.D, wl.W, wl.k, wl.B
+    vx = synth.make_verify_inputs(B, VERIFY["P"], VERIFY["Hq"], VERIFY["Hkv"], VERIFY["hd"],
+                                  seed=wl.seeds[0])
+    vq, vkp, vvp, vkt, vvt = (up16(vx[n]) for n in ("q", "k_prefix", "v_prefix", "k_tree",
+                                                      "v_tree"))
+    scale = 1.0 / math.sqrt(VERIFY["hd"])
+
+    pool = dict(pool_tok=torch.empty((R, D, W), dtype=torch.int32, device=dev),
+                pool_parent=torch.empty((R, D, W), dtype=torch.int32, device=dev),
+                pool_score=torch.empty((R, D, W), dtype=torch.float32, device=dev),
+                n_valid=torch.empty((R, D), dtype=torch.int32, device=dev))
+    sel = dict(sel_node=torch.empty((R, B), dtype=torch.int32, device=dev),
+               sel_parent=torch.empty((R, B), dtype=torch.int32, device=dev),
+               sel_depth=torch.empty((R, B), dtype=torch.int32, device=dev),
+               n_sel=torch.empty((R,), dtype=torch.int32, device=dev))
+    mask = torch.empty((R, B, (B + 31) // 32), dtype=torch.int32, device=dev)
+    ws = torch.empty(A.build_supertree_workspace_size(head, R, D, W, k), dtype=torch.uint8,
+                     device=dev)
+    aws = torch.empty(A.tree_attention_workspace_size(B, VERIFY["P"], VERIFY["Hq"],
+                                                      VERIFY["Hkv"], VERIFY["hd"]),
+                      dtype=torch.uint8, device=dev)
+    aout = torch.empty((B, VERIFY["Hq"], VERIFY["hd"]), dtype=torch.float32, device=dev)
+
+    def step():
+        A.build_supertree(head, h, s0, root, D, W, k, wl.T, workspace=ws, out=pool)
+        A.prune_topB(pool["pool_score"], pool["pool_parent"], pool["n_valid"], B, wl.beta,
+                     out=sel)
+        A.build_tree_mask(sel["sel_parent"], sel["n_sel"], out=mask)
+        # verification layer over request 0's pruned tree (rows >= n_sel are empty)
+        A.tree_attention_verify(vq, vkp, vvp, vkt, vvt, mask[0], scale, workspace=aws, out=aout)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    def timed_region(per_kernel: bool):
+        A.timing_reset()
+        A.timing_enable(per_kernel)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        A.timing_enable(False)
+        return e0.elapsed_time(e1), wall
+
+    ev_ms, wall = timed_region(False)
+    ms_per_step = max(ev_ms, wall * 1e3) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (events {ev_ms:.1f} ms, "
+        f"wall {wall * 1e3:.1f} ms)")
+    # the same steps again with every library launch bracketed by HIP events
+    pk_ms, _ = timed_region(True)
+    kern = {}
+    for name in ("gemm1", "gemm2", "head", "merge_select"):
+        tot, n = A.timing_read(name)
+        kern[name] = dict(launches=n, avg_us=(tot * 1e3 / n) if n else None)
+    head_us = kern["head"]["avg_us"]
+    wbytes = 2 if wl.wdtype == "bf16" else 4
+    head_bytes = wbytes * wl.d * wl.V          # the output head, streamed once per launch
+    achieved = head_bytes / (head_us * 1e-6) / 1e9
+    log(f"[bench] head kernel {head_us:.1f} us/launch -> {achieved:.0f} GB/s; "
+        f"per-kernel timed region {pk_ms / args.steps:.3f} ms/step")
+
+    builds_per_s = R * 1e3 / ms_per_step
+    # weights streamed per step: U (d V) + W1 and W2 (8 d^2) per depth, shared by R requests
+    bytes_per_step = D * wbytes * (wl.d * wl.V + 8 * wl.d * wl.d)
+    res = {
+        "metric": METRIC,
+        "value": round(builds_per_s, 3),
+        "unit": "builds/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.wdtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "D": D, "W": W, "k": k, "V": wl.V, "d": wl.d, "R": R,
+                   "B": B, "beta": wl.beta, "T": wl.T,
+                   "verify_layer": dict(VERIFY, n_tree=B)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "corrected-logit head (k_head_bf16)",
+                     "bytes_per_launch": head_bytes},
+        "kernels_us": {n: (round(v["avg_us"], 2) if v["avg_us"] else None) for n, v in kern.items()},
+        "weight_bytes_per_step": bytes_per_step,
+        "step_weight_stream_gbs": round(bytes_per_step / (ms_per_step * 1e-3) / 1e9, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, hw, req, args.cpu_builds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(wl, hw, req, nbuilds):
+    """The fp64 oracle as it stands, on this host's cores, on a bounded sample:
+    `nbuilds` full builds of request 0 (all D depths) plus prune and mask."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import dartree_oracle as O
+    t0 = time.time()
+    ohead = O.OracleHead(hw.wdtype, hw.E, hw.W1t, hw.W2t, hw.Ut)
+    prep = time.time() - t0
+    times = []
+    for _ in range(nbuilds):
+        t1 = time.perf_counter()
+        tree = O.build_supertree(ohead, req.h[0], req.s0[0], int(req.root_tok[0]), wl.D, wl.W,
+                                 wl.k, wl.T)
+        vt = O.prune_topB(tree.score, tree.parent, tree.n_valid, wl.B, wl.beta)
+        O.tree_mask(vt.parent, vt.n, wl.B)
+        times.append(time.perf_counter() - t1)
+    info = threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] or [1])
+    med = sorted(times)[len(times) // 2]
+    log(f"[bench] oracle build {med:.2f}s (weights widened in {prep:.1f}s), {cores} threads")
+    return {"value": round(1.0 / med, 5), "unit": "builds/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nbuilds} full fp64 oracle build(s) of request 0 ({wl.name}: D={wl.D}, "
+                      f"W={wl.W}, k={wl.k}) + prune + mask; median; weight widening "
+                      f"({prep:.1f}s) excluded",
+            "blas": ",".join(sorted({i.get('internal_api', '?') for i in info}))}
+
+
+if __name__ == "__main__":
+    main()

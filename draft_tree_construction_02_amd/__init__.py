@@ -1,0 +1,8 @@
+"""MI355X (gfx950) library for DARTree's depth-wise batched draft-supertree
+construction, deferred top-B pruning, the ancestor mask and one tree-attention
+verification layer.  Compute runs in libdartree.so (HIP); this package holds
+the ctypes binding, the build script and the seeded synthetic inputs."""
+from ._abi import (  # noqa: F401
+    DartreeError, Head, build_supertree, build_supertree_workspace_size, build_tree_mask,
+    corrected_topk, head_step_workspace_size, lib, prune_topB, state_update, timing_enable,
+    timing_read, timing_reset, tree_attention_verify, tree_attention_workspace_size)

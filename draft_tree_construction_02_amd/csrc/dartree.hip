@@ -1,0 +1,437 @@
+// C ABI of the library: argument validation, workspace layout and the
+// per-depth launch sequence of depth-wise batched supertree construction.
+//
+// One depth t (one batched head call over all R * W surviving branches):
+//   gemm1  H  = GELU((E[tok] + h_t) W1)             split-K, last split reduces
+//   gemm2  s' = s_parent + H W2                      split-K, last split reduces
+//   head   per vocabulary tile: (max, sum exp) and top-k of s' U / T
+//   merge  per row: log-sum-exp and top-k over all tiles -> children, logp
+//   beam   per request: global top-W of parent score + logp, carry states
+// Everything is enqueued on the caller's stream; nothing synchronises.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/dartree.h"
+#include "launch.hpp"
+
+using namespace dt;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+int padded_rows(int rows) {
+  if (rows <= 16) return 16;
+  if (rows <= 32) return 32;
+  if (rows <= 64) return 64;
+  return 128;
+}
+
+int kmax_for(int k, bool greedy) {
+  if (greedy || k == 1) return 1;
+  if (k <= 4) return 4;
+  if (k <= 8) return 8;
+  return 16;
+}
+
+// Largest divisor s of nk with tiles * s <= 768 (enough workgroups to cover
+// 256 CUs a few times without making each split trivially short).
+int choose_splits(int nk, int tiles) {
+  int best = 1;
+  for (int s = 1; s <= nk; ++s)
+    if (nk % s == 0 && (long)tiles * s <= 768) best = s;
+  return best;
+}
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((char*)b) {}
+  template <class T>
+  T* take(size_t n) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += align_up(n * sizeof(T));
+    return p;
+  }
+};
+
+bool head_ok(const dt_head* h) {
+  if (!h || !h->E || !h->W1t || !h->W2t || !h->Ut) return false;
+  if (h->V < 1 || h->d < 1) return false;
+  if (h->wdtype == DT_BF16) return h->d % 128 == 0;
+  if (h->wdtype == DT_F32) return h->d % 32 == 0;
+  return false;
+}
+
+// Layout of the state-update + head workspace for Mp rows.
+struct StepWs {
+  float* part;
+  uint32_t* counters;
+  float* H;
+  float2* ms_part;
+  uint64_t* key_part;
+  int32_t* cand_tok;
+  float* cand_lp;
+  float* lse;
+  int32_t* tok[2];
+  float* score[2];
+  int32_t* src[2];
+  float* S[2];
+  int Mp, tiles1, tiles2, tilesV, splits1, splits2, ncounters, kt;
+};
+
+StepWs carve_step(Carver& c, const dt_head* h, int rows, int k, bool keep_states) {
+  StepWs w{};
+  const int bf = h->wdtype == DT_BF16;
+  const int d = h->d, V = h->V;
+  const int TN = gemm_tile_n(bf), KC = gemm_k_chunk(bf, 0);
+  w.Mp = padded_rows(rows);
+  w.tiles1 = (4 * d + TN - 1) / TN;
+  w.tiles2 = (d + TN - 1) / TN;
+  w.tilesV = (V + head_tile_n(bf) - 1) / head_tile_n(bf);
+  w.splits1 = choose_splits(d / KC, w.tiles1);
+  w.splits2 = choose_splits(4 * d / KC, w.tiles2);
+  w.ncounters = w.tiles1 > w.tiles2 ? w.tiles1 : w.tiles2;
+  w.kt = k;
+  const size_t part1 = (size_t)w.splits1 * w.Mp * 4 * d;
+  const size_t part2 = (size_t)w.splits2 * w.Mp * d;
+  w.part = c.take<float>(part1 > part2 ? part1 : part2);
+  w.counters = c.take<uint32_t>(w.ncounters);
+  w.H = c.take<float>((size_t)w.Mp * 4 * d);
+  w.ms_part = c.take<float2>((size_t)w.Mp * w.tilesV);
+  w.key_part = c.take<uint64_t>((size_t)w.Mp * w.tilesV * k);
+  w.cand_tok = c.take<int32_t>((size_t)w.Mp * k);
+  w.cand_lp = c.take<float>((size_t)w.Mp * k);
+  w.lse = c.take<float>(w.Mp);
+  for (int i = 0; i < 2; ++i) {
+    w.tok[i] = c.take<int32_t>(w.Mp);
+    w.score[i] = c.take<float>(w.Mp);
+    w.src[i] = c.take<int32_t>(w.Mp);
+    w.S[i] = keep_states ? c.take<float>((size_t)w.Mp * d) : nullptr;
+  }
+  return w;
+}
+
+// ---------------------------------------------------------------- timing
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> free_ev;
+  struct Rec { int cls; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  double total_ms[DT_K_COUNT] = {};
+  int64_t count[DT_K_COUNT] = {};
+} g_timing;
+
+hipEvent_t take_event() {
+  if (!g_timing.free_ev.empty()) {
+    hipEvent_t e = g_timing.free_ev.back();
+    g_timing.free_ev.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` bracketed by events when timing is on.
+template <class F>
+hipError_t timed(int cls, hipStream_t st, F&& launch) {
+  if (!g_timing.on) return launch();
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) return launch();
+  (void)hipEventRecord(a, st);
+  hipError_t e = launch();
+  (void)hipEventRecord(b, st);
+  g_timing.pending.push_back({cls, a, b});
+  return e;
+}
+
+void collect_pending() {
+  for (auto& r : g_timing.pending) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      g_timing.total_ms[r.cls] += ms;
+      g_timing.count[r.cls] += 1;
+    }
+    g_timing.free_ev.push_back(r.a);
+    g_timing.free_ev.push_back(r.b);
+  }
+  g_timing.pending.clear();
+}
+
+// ---------------------------------------------------------------- one depth
+struct DepthIo {
+  const float* s_prev;      // residual source (rows indexed by src)
+  const int32_t* tok;       // tokens entering the update
+  const int32_t* src;       // residual row of each row (-1 none)
+  const float* h;           // hidden base for this depth
+  long h_req_stride;
+  int rpr;
+  int rows;
+  float* s_out;             // updated states [Mp or rows][d]
+};
+
+hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hipStream_t st) {
+  const int bf = hd->wdtype == DT_BF16, d = hd->d;
+  GemmArgs g1;
+  g1.a.gather = 1;
+  g1.a.E = hd->E;
+  g1.a.ldE = d;
+  g1.a.e_bf16 = bf;
+  g1.a.tok = io.tok;
+  g1.a.h = io.h;
+  g1.a.h_req_stride = io.h_req_stride;
+  g1.a.rpr = io.rpr;
+  g1.a.rows = io.rows;
+  g1.Wt = hd->W1t;
+  g1.w_bf16 = bf;
+  g1.N = 4 * d;
+  g1.K = d;
+  g1.Mp = w.Mp;
+  g1.splits = w.splits1;
+  g1.part = w.part;
+  g1.counters = w.counters;
+  g1.epi = EPI_GELU;
+  g1.out = w.H;
+  hipError_t e = timed(DT_K_GEMM1, st, [&] { return launch_gemm(g1, st); });
+  if (e != hipSuccess) return e;
+
+  GemmArgs g2;
+  g2.a.a = w.H;
+  g2.a.lda = 4 * d;
+  g2.a.rows = io.rows;
+  g2.Wt = hd->W2t;
+  g2.w_bf16 = bf;
+  g2.N = d;
+  g2.K = 4 * d;
+  g2.Mp = w.Mp;
+  g2.splits = w.splits2;
+  g2.part = w.part;
+  g2.counters = w.counters;
+  g2.epi = EPI_RESID;
+  g2.out = io.s_out;
+  g2.s_prev = io.s_prev;
+  g2.src_row = io.src;
+  return timed(DT_K_GEMM2, st, [&] { return launch_gemm(g2, st); });
+}
+
+hipError_t run_head(const dt_head* hd, const StepWs& w, const float* s, int rows, int k, float T,
+                    int32_t* cand_tok, float* cand_lp, float* lse, hipStream_t st) {
+  const bool greedy = T == 0.f;
+  HeadArgs p;
+  p.a.a = s;
+  p.a.lda = hd->d;
+  p.a.rows = rows;
+  p.Ut = hd->Ut;
+  p.w_bf16 = hd->wdtype == DT_BF16;
+  p.V = hd->V;
+  p.d = hd->d;
+  p.Mp = w.Mp;
+  p.kmax = kmax_for(k, greedy);
+  p.k = greedy ? 1 : k;
+  p.inv_T = greedy ? 1.f : (float)(1.0 / (double)T);
+  p.greedy = greedy;
+  p.ms_part = w.ms_part;
+  p.key_part = w.key_part;
+  hipError_t e = timed(DT_K_HEAD, st, [&] { return launch_head(p, st); });
+  if (e != hipSuccess) return e;
+  return timed(DT_K_MERGE, st, [&] {
+    return launch_merge(w.ms_part, w.key_part, rows, w.tilesV, p.k, k, p.kmax, greedy,
+                        cand_tok, cand_lp, lse, st);
+  });
+}
+
+}  // namespace
+
+// ============================================================================
+extern "C" {
+
+const char* dartree_status_string(int s) {
+  switch (s) {
+    case DT_OK: return "ok";
+    case DT_EINVAL: return "invalid argument";
+    case DT_EWORKSPACE: return "workspace missing or too small";
+    case DT_EUNSUPPORTED: return "outside this build's limits";
+    case DT_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int dartree_version(void) { return (1 << 16) | 0; }
+
+static int build_args_ok(const dt_head* head, int R, int D, int W, int k) {
+  if (!head_ok(head)) return DT_EINVAL;
+  if (R < 1 || D < 1 || W < 1 || k < 1 || k > head->V) return DT_EINVAL;
+  if (D > DT_MAX_DEPTH || k > DT_MAX_K || (long)R * W > DT_MAX_ROWS ||
+      (long)W * k > DT_MAX_CAND || (long)D * W > DT_MAX_POOL)
+    return DT_EUNSUPPORTED;
+  return DT_OK;
+}
+
+size_t build_supertree_workspace_size(const dt_head* head, int R, int D, int W, int k) {
+  if (build_args_ok(head, R, D, W, k) != DT_OK) return 0;
+  Carver c(nullptr);
+  carve_step(c, head, R * W, k, true);
+  return c.off;
+}
+
+int build_supertree(const dt_head* head, const float* h, const float* s0, const int32_t* root_tok,
+                    int R, int D, int W, int k, float T, int32_t* pool_tok, int32_t* pool_parent,
+                    float* pool_score, int32_t* n_valid, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  int rc = build_args_ok(head, R, D, W, k);
+  if (rc != DT_OK) return rc;
+  if (!h || !s0 || !root_tok || !pool_tok || !pool_parent || !pool_score || !n_valid)
+    return DT_EINVAL;
+  if (!(T >= 0.f) || !isfinite(T)) return DT_EINVAL;
+  const size_t need = build_supertree_workspace_size(head, R, D, W, k);
+  if (!workspace || workspace_bytes < need) return DT_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  Carver c(workspace);
+  StepWs w = carve_step(c, head, R * W, k, true);
+  const int d = head->d, rows = R * W;
+  const bool greedy = T == 0.f;
+
+  hipError_t e = launch_beam_init(R, W, w.Mp, root_tok, w.tok[0], w.score[0], w.src[0],
+                                  w.counters, w.ncounters, st);
+  for (int t = 0; t < D && e == hipSuccess; ++t) {
+    const int cur = t & 1, nxt = cur ^ 1;
+    DepthIo io;
+    io.s_prev = t == 0 ? s0 : w.S[nxt];
+    io.tok = w.tok[cur];
+    io.src = w.src[cur];
+    io.h = h + (long)t * d;
+    io.h_req_stride = (long)D * d;
+    io.rpr = W;
+    io.rows = rows;
+    io.s_out = w.S[cur];
+    e = run_update(head, w, io, st);
+    if (e != hipSuccess) break;
+    e = run_head(head, w, w.S[cur], rows, k, T, w.cand_tok, w.cand_lp, w.lse, st);
+    if (e != hipSuccess) break;
+    BeamArgs b;
+    b.R = R; b.W = W; b.k = k; b.D = D; b.t = t; b.greedy = greedy;
+    b.cand_tok = w.cand_tok;
+    b.cand_lp = w.cand_lp;
+    b.score_in = w.score[cur];
+    b.n_valid = n_valid;
+    b.pool_tok = pool_tok;
+    b.pool_parent = pool_parent;
+    b.pool_score = pool_score;
+    b.tok_out = w.tok[nxt];
+    b.score_out = w.score[nxt];
+    b.src_out = w.src[nxt];
+    b.Mp = w.Mp;
+    e = timed(DT_K_MERGE, st, [&] { return launch_beam_select(b, st); });
+  }
+  return e == hipSuccess ? DT_OK : DT_EHIP;
+}
+
+size_t head_step_workspace_size(const dt_head* head, int rows, int k) {
+  if (!head_ok(head) || rows < 1 || rows > DT_MAX_ROWS || k < 1 || k > DT_MAX_K ||
+      k > head->V)
+    return 0;
+  Carver c(nullptr);
+  carve_step(c, head, rows, k, false);
+  return c.off;
+}
+
+int state_update(const dt_head* head, const float* s_in, const int32_t* tok, const float* h,
+                 int rows, float* s_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!head_ok(head) || !s_in || !tok || !h || !s_out) return DT_EINVAL;
+  if (rows < 1) return DT_EINVAL;
+  if (rows > DT_MAX_ROWS) return DT_EUNSUPPORTED;
+  if (s_in == s_out) return DT_EINVAL;
+  const size_t need = head_step_workspace_size(head, rows, 1);
+  if (!workspace || workspace_bytes < need) return DT_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  Carver c(workspace);
+  StepWs w = carve_step(c, head, rows, 1, false);
+  hipError_t e = launch_fill_rows(rows, w.Mp, tok, w.tok[0], w.src[0], w.counters, w.ncounters, st);
+  if (e == hipSuccess) {
+    DepthIo io;
+    io.s_prev = s_in;
+    io.tok = w.tok[0];
+    io.src = w.src[0];
+    io.h = h;
+    io.h_req_stride = 0;
+    io.rpr = 1;
+    io.rows = rows;
+    io.s_out = s_out;
+    e = run_update(head, w, io, st);
+  }
+  return e == hipSuccess ? DT_OK : DT_EHIP;
+}
+
+int corrected_topk(const dt_head* head, const float* s, int rows, int k, float T,
+                   int32_t* cand_tok, float* cand_lp, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!head_ok(head) || !s || !cand_tok || !cand_lp || !lse) return DT_EINVAL;
+  if (rows < 1 || k < 1 || k > head->V) return DT_EINVAL;
+  if (rows > DT_MAX_ROWS || k > DT_MAX_K) return DT_EUNSUPPORTED;
+  if (!(T >= 0.f) || !isfinite(T)) return DT_EINVAL;
+  const size_t need = head_step_workspace_size(head, rows, k);
+  if (!workspace || workspace_bytes < need) return DT_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  Carver c(workspace);
+  StepWs w = carve_step(c, head, rows, k, false);
+  hipError_t e = run_head(head, w, s, rows, k, T, cand_tok, cand_lp, lse, st);
+  return e == hipSuccess ? DT_OK : DT_EHIP;
+}
+
+int prune_topB(const float* pool_score, const int32_t* pool_parent, const int32_t* n_valid, int R,
+               int D, int W, int B, float beta, int32_t* sel_node, int32_t* sel_parent,
+               int32_t* sel_depth, int32_t* n_sel, void* stream) {
+  if (!pool_score || !pool_parent || !n_valid || !sel_node || !sel_parent || !sel_depth || !n_sel)
+    return DT_EINVAL;
+  if (R < 1 || D < 1 || W < 1 || B < 1 || (long)B > (long)D * W) return DT_EINVAL;
+  if (!(beta <= 0.f) || !isfinite(beta)) return DT_EINVAL;
+  if ((long)D * W > DT_MAX_POOL || B > DT_MAX_B || D > DT_MAX_DEPTH) return DT_EUNSUPPORTED;
+  hipError_t e = launch_prune(pool_score, pool_parent, n_valid, R, D, W, B, beta, sel_node,
+                              sel_parent, sel_depth, n_sel, (hipStream_t)stream);
+  return e == hipSuccess ? DT_OK : DT_EHIP;
+}
+
+int build_tree_mask(const int32_t* sel_parent, const int32_t* n_sel, int R, int B,
+                    uint32_t* mask, void* stream) {
+  if (!sel_parent || !n_sel || !mask) return DT_EINVAL;
+  if (R < 1 || B < 1) return DT_EINVAL;
+  if (B > DT_MAX_B) return DT_EUNSUPPORTED;
+  hipError_t e = launch_mask(sel_parent, n_sel, R, B, mask, (hipStream_t)stream);
+  return e == hipSuccess ? DT_OK : DT_EHIP;
+}
+
+int dartree_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  g_timing.on = enable != 0;
+  return DT_OK;
+}
+
+int dartree_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  collect_pending();
+  for (int i = 0; i < DT_K_COUNT; ++i) {
+    g_timing.total_ms[i] = 0.0;
+    g_timing.count[i] = 0;
+  }
+  return DT_OK;
+}
+
+int dartree_timing_read(int cls, double* total_ms, int64_t* launches) {
+  if (cls < 0 || cls >= DT_K_COUNT || !total_ms || !launches) return DT_EINVAL;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  collect_pending();
+  *total_ms = g_timing.total_ms[cls];
+  *launches = g_timing.count[cls];
+  return DT_OK;
+}
+
+}  // extern "C"

@@ -49,9 +49,9 @@ typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
 
 /* Limits of this build (checked on the host). */
 #define DT_MAX_K 16         /* children per branch                              */
-#define DT_MAX_ROWS 256     /* R * W: branch rows evaluated per head call        */
+#define DT_MAX_ROWS 128     /* R * W: branch rows evaluated per head call        */
 #define DT_MAX_CAND 4096    /* W * k candidates per request and depth           */
-#define DT_MAX_POOL 8192    /* D * W pool nodes per request                      */
+#define DT_MAX_POOL 4096    /* D * W pool nodes per request                      */
 #define DT_MAX_B 1024       /* verification budget per request                   */
 #define DT_MAX_DEPTH 64
 
@@ -68,7 +68,7 @@ typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
  *     Ut  [V][d]      U transposed (vocab-major: a vocabulary tile is one
  *                     contiguous block)
  * wdtype DT_BF16: all four are bfloat16; DT_F32: all four are float32.
- * d must be a multiple of 128 for DT_BF16 and of 4 for DT_F32.
+ * d must be a multiple of 128 for DT_BF16 and of 32 for DT_F32.
  */
 typedef struct {
   int32_t d;

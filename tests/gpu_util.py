@@ -1,0 +1,50 @@
+"""Helpers shared by the GPU tests: upload seeded inputs, run the library,
+bring results back to numpy."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from draft_tree_construction_02_amd import _abi as A
+from draft_tree_construction_02_amd import synth
+from oracle import dartree_oracle as O
+
+DEV = "cuda:0"
+
+
+def dev_weights(hw: synth.HeadWeights) -> A.Head:
+    def up(a):
+        if hw.wdtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return A.Head(up(hw.E), up(hw.W1t), up(hw.W2t), up(hw.Ut))
+
+
+def oracle_head(hw: synth.HeadWeights, cache_u=True) -> O.OracleHead:
+    return O.OracleHead(hw.wdtype, hw.E, hw.W1t, hw.W2t, hw.Ut, cache_u=cache_u)
+
+
+def dev_requests(req: synth.Requests):
+    return (torch.from_numpy(req.h).to(DEV), torch.from_numpy(req.s0).to(DEV),
+            torch.from_numpy(req.root_tok).to(DEV))
+
+
+def to_np(d: dict) -> dict:
+    return {k: v.cpu().numpy() for k, v in d.items()}
+
+
+def bf16_dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def tolerances(wdtype: str, ymax: float = 8.0):
+    """(score tolerance, near-tie gap tau) for a head dtype.
+
+    bf16 heads: 2e-3 absolute on log-probabilities and path scores, tau = 2 tol.
+    fp32 heads: fp32 rounding of a logit is relative to its size, so the
+    tolerance is 1e-5 for logits up to 8 in magnitude and grows with them.
+    """
+    if wdtype == "bf16":
+        return 2e-3, 4e-3
+    tol = 1e-5 * max(1.0, ymax / 8.0)
+    return tol, 2 * tol

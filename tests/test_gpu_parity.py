@@ -1,0 +1,218 @@
+"""GPU parity of every hot-path kernel against the fp64 oracle, at sizes the
+oracle finishes in seconds that still span several tiles and a ragged tail.
+
+The library is called through the C ABI (ctypes binding); the oracle sees the
+same seeded inputs.  Discrete outputs must match exactly except where the
+oracle's own fp64 score gap is below tau (counted); scores within tol.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from draft_tree_construction_02_amd import _abi as A
+from draft_tree_construction_02_amd import synth
+from oracle import dartree_oracle as O
+from oracle import parity as PAR
+from tests.gpu_util import (DEV, bf16_dev, dev_requests, dev_weights, oracle_head, to_np,
+                            tolerances)
+
+pytestmark = pytest.mark.gpu
+
+
+def small_cases():
+    w = synth.workloads()
+    return {
+        # the tiny fp32 workload, exactly as specified
+        "tiny": w["tiny"],
+        # bf16 head, vocabulary with a ragged last tile (5000 = 39*128 + 8)
+        "bf16_T1": synth.Workload("bf16_T1", V=5000, d=256, wdtype="bf16", D=5, W=8, k=4, B=24,
+                                  beta=-0.05, T=1.0, R=2, seeds=(0, 1)),
+        "bf16_T0": synth.Workload("bf16_T0", V=5000, d=256, wdtype="bf16", D=5, W=8, k=4, B=4,
+                                  beta=0.0, T=0.0, R=2, seeds=(0, 1)),
+        "bf16_ragged_rows": synth.Workload("bf16_ragged_rows", V=3001, d=384, wdtype="bf16", D=4,
+                                           W=6, k=3, B=13, beta=0.0, T=0.7, R=3, seeds=(3, 4, 5)),
+        "bf16_k16": synth.Workload("bf16_k16", V=2048, d=128, wdtype="bf16", D=3, W=20, k=16,
+                                   B=40, beta=-0.2, T=1.3, R=1, seeds=(7,)),
+        "f32_wide": synth.Workload("f32_wide", V=700, d=96, wdtype="f32", D=4, W=40, k=5, B=100,
+                                   beta=-0.01, T=1.0, R=2, seeds=(2, 9)),
+    }
+
+
+_cache = {}
+
+
+def case_inputs(wl):
+    if wl.name not in _cache:
+        hw, req = synth.make_workload_inputs(wl)
+        _cache[wl.name] = (hw, req, dev_weights(hw), oracle_head(hw))
+    return _cache[wl.name]
+
+
+@pytest.mark.parametrize("name", list(small_cases()))
+def test_build_prune_mask_match_oracle(name):
+    wl = small_cases()[name]
+    print(f"case {name}", flush=True)
+    hw, req, head, ohead = case_inputs(wl)
+    tol, tau = tolerances(wl.wdtype)
+    h, s0, root = dev_requests(req)
+    out = A.build_supertree(head, h, s0, root, wl.D, wl.W, wl.k, wl.T)
+    sel = A.prune_topB(out["pool_score"], out["pool_parent"], out["n_valid"], wl.B, wl.beta)
+    mask = A.build_tree_mask(sel["sel_parent"], sel["n_sel"])
+    torch.cuda.synchronize()
+    pool, sel, mask = to_np(out), to_np(sel), mask.cpu().numpy().view(np.uint32)
+    total_exempt = 0
+    for r in range(wl.R):
+        dev = dict(tok=pool["pool_tok"][r], parent=pool["pool_parent"][r],
+                   score=pool["pool_score"][r], n_valid=pool["n_valid"][r])
+        rep = PAR.check_build(ohead, req.h[r], req.s0[r], int(req.root_tok[r]), wl.D, wl.W,
+                              wl.k, wl.T, dev, tol, tau)
+        assert rep.ok, rep.failures[:5]
+        dsel = dict(node=sel["sel_node"][r], parent=sel["sel_parent"][r],
+                    depth=sel["sel_depth"][r], n=sel["n_sel"][r])
+        PAR.check_prune(rep.forced_score, dev["parent"], dev["n_valid"], wl.B, wl.beta, dsel,
+                        tau, rep)
+        assert rep.ok, rep.failures[:5]
+        bad = PAR.check_mask(dsel["parent"], dsel["n"], wl.B, mask[r])
+        assert not bad, bad
+        if rep.exemptions == 0:
+            ora = O.build_supertree(ohead, req.h[r], req.s0[r], int(req.root_tok[r]), wl.D,
+                                    wl.W, wl.k, wl.T)
+            assert not PAR.compare_exact(ora, dev, tol)
+            vt = O.prune_topB(ora.score, ora.parent, ora.n_valid, wl.B, wl.beta)
+            assert np.array_equal(dsel["node"][:vt.n], vt.node)
+            assert np.array_equal(dsel["parent"][:vt.n], vt.parent)
+            assert np.array_equal(dsel["depth"][:vt.n], vt.depth)
+        total_exempt += rep.exemptions
+    print(f"{name}: exemptions {total_exempt}", flush=True)
+
+
+def test_build_is_deterministic():
+    wl = small_cases()["bf16_T1"]
+    hw, req, head, _ = case_inputs(wl)
+    h, s0, root = dev_requests(req)
+    ref = to_np(A.build_supertree(head, h, s0, root, wl.D, wl.W, wl.k, wl.T))
+    for _ in range(4):
+        got = to_np(A.build_supertree(head, h, s0, root, wl.D, wl.W, wl.k, wl.T))
+        for key in ref:
+            assert np.array_equal(ref[key].view(np.uint8), got[key].view(np.uint8)), key
+
+
+@pytest.mark.parametrize("name,rows,k,T", [("bf16_T1", 20, 8, 1.0), ("bf16_T1", 16, 4, 0.5),
+                                           ("bf16_T1", 33, 16, 2.0), ("bf16_T0", 7, 8, 0.0),
+                                           ("tiny", 4, 4, 1.0), ("f32_wide", 70, 5, 1.0)])
+def test_corrected_topk_matches_oracle(name, rows, k, T):
+    wl = small_cases()[name]
+    hw, _, head, ohead = case_inputs(wl)
+    tol, tau = tolerances(wl.wdtype)
+    g = np.random.default_rng(rows * 31 + k)
+    s = (g.standard_normal((rows, wl.d)) * 2.0).astype(np.float32)
+    tok, lp, lse = A.corrected_topk(head, torch.from_numpy(s).to(DEV), k, T)
+    tok, lp, lse = tok.cpu().numpy(), lp.cpu().numpy(), lse.cpu().numpy()
+    z = ohead.logits(s.astype(np.float64))
+    tol, tau = tolerances(wl.wdtype, float(np.max(np.abs(z))) / (T if T > 0 else 1.0))
+    exempt = 0
+    for i in range(rows):
+        olp = O.log_softmax_T(z[i], T)
+        otok, olps = O.topk_children(olp, k)
+        if T == 0.0:
+            assert tok[i, 0] == otok[0] or z[i, otok[0]] - z[i, tok[i, 0]] <= tau
+            assert lp[i, 0] == 0.0 and np.all(tok[i, 1:] == -1) and np.all(np.isneginf(lp[i, 1:]))
+            assert abs(lse[i] - z[i].max()) <= tol * max(1.0, abs(z[i].max()))
+            continue
+        y = z[i] / T
+        olse = y.max() + math.log(np.sum(np.exp(y - y.max())))
+        assert abs(lse[i] - olse) <= tol
+        assert len(set(tok[i].tolist())) == k
+        for j in range(k):
+            t = int(tok[i, j])
+            assert abs(lp[i, j] - olp[t]) <= tol
+            if t not in set(otok.tolist()):
+                assert olps[-1] - olp[t] <= tau
+                exempt += 1
+        assert np.all(np.diff(lp[i]) <= 0)
+        if exempt == 0:
+            assert tok[i].tolist() == otok.tolist()
+    print(f"topk {name} exemptions {exempt}")
+
+
+@pytest.mark.parametrize("name,rows", [("bf16_T1", 20), ("bf16_ragged_rows", 18), ("tiny", 4),
+                                       ("f32_wide", 80)])
+def test_state_update_matches_oracle(name, rows):
+    wl = small_cases()[name]
+    hw, _, head, ohead = case_inputs(wl)
+    g = np.random.default_rng(rows)
+    s = g.standard_normal((rows, wl.d)).astype(np.float32)
+    tok = g.integers(0, wl.V, rows).astype(np.int32)
+    hvec = g.standard_normal(wl.d).astype(np.float32)
+    got = A.state_update(head, torch.from_numpy(s).to(DEV), torch.from_numpy(tok).to(DEV),
+                         torch.from_numpy(hvec).to(DEV)).cpu().numpy()
+    want = O.state_update(ohead, s, tok, hvec)
+    atol = 1e-4 if wl.wdtype == "bf16" else 1e-5
+    assert np.max(np.abs(got - want)) <= atol
+
+
+def _random_pool(g, D, W, integer):
+    score = np.full((D, W), -np.inf, np.float32)
+    parent = np.full((D, W), -1, np.int32)
+    nv = np.zeros(D, np.int32)
+    prev = 1
+    for t in range(D):
+        n = int(g.integers(1, W + 1)) if prev else 0
+        nv[t] = n
+        for j in range(n):
+            p = int(g.integers(0, prev)) if t else -1
+            base = 0.0 if t == 0 else float(score[t - 1, p])
+            step = float(g.integers(0, 4)) if integer else float(g.random() * 3)
+            score[t, j] = base - step
+            parent[t, j] = p
+        # slots in non-increasing score order, as the builder emits them
+        order = np.argsort(-score[t, :n], kind="stable")
+        score[t, :n] = score[t, :n][order]
+        parent[t, :n] = parent[t, :n][order]
+        prev = n
+    return score, parent, nv
+
+
+@pytest.mark.parametrize("integer", [True, False])
+def test_prune_and_mask_match_oracle_on_random_pools(integer):
+    g = np.random.default_rng(42 + integer)
+    R, D, W = 6, 7, 9
+    pools = [_random_pool(g, D, W, integer) for _ in range(R)]
+    sc = np.stack([p[0] for p in pools]); pa = np.stack([p[1] for p in pools])
+    nv = np.stack([p[2] for p in pools])
+    for B, beta in ((1, 0.0), (5, -0.5), (17, 0.0), (40, -1.0), (63, -0.25)):
+        sel = A.prune_topB(torch.from_numpy(sc).to(DEV), torch.from_numpy(pa).to(DEV),
+                           torch.from_numpy(nv).to(DEV), B, beta)
+        mask = A.build_tree_mask(sel["sel_parent"], sel["n_sel"]).cpu().numpy().view(np.uint32)
+        sel = to_np(sel)
+        for r in range(R):
+            vt = O.prune_topB(sc[r].astype(np.float64), pa[r], nv[r], B, beta)
+            n = int(sel["n_sel"][r])
+            assert n == vt.n
+            assert np.array_equal(sel["sel_node"][r, :n], vt.node)
+            assert np.array_equal(sel["sel_parent"][r, :n], vt.parent)
+            assert np.array_equal(sel["sel_depth"][r, :n], vt.depth)
+            assert np.all(sel["sel_node"][r, n:] == -1)
+            assert np.array_equal(mask[r], O.tree_mask(vt.parent, vt.n, B))
+
+
+@pytest.mark.parametrize("n,P,Hq,Hkv", [(37, 100, 8, 2), (128, 0, 4, 4), (70, 333, 32, 8)])
+def test_tree_attention_matches_oracle(n, P, Hq, Hkv):
+    hd = 128
+    g = np.random.default_rng(n + P)
+    par = np.array([-1] + [int(g.integers(-1, i)) for i in range(1, n)], np.int32)
+    par = np.minimum(par, np.arange(n) - 1)
+    mask = O.tree_mask(par, n, n)
+    x = synth.make_verify_inputs(n, P, Hq, Hkv, hd, seed=n)
+    scale = 1.0 / math.sqrt(hd)
+    args = [bf16_dev(x[k]) for k in ("q", "k_prefix", "v_prefix", "k_tree", "v_tree")]
+    got = A.tree_attention_verify(*args, torch.from_numpy(mask.view(np.int32)).to(DEV), scale)
+    got = got.cpu().numpy()
+    f = lambda b: synth.bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
+    want = O.tree_attention(f(x["q"]), f(x["k_prefix"]), f(x["v_prefix"]), f(x["k_tree"]),
+                            f(x["v_tree"]), mask, n, scale)
+    err = np.max(np.abs(got - want))
+    assert err <= 1e-2 * np.max(np.abs(want)), err
+    assert np.linalg.norm(got - want) <= 1e-2 * np.linalg.norm(want)
