@@ -75,6 +75,10 @@ def main():
         return up16(a) if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     head = A.Head(up(hw.E), up(hw.W1t), up(hw.W2t), up(hw.Ut))
+    if wl.wdtype == "bf16":
+        # weights are packed once, as at model load; the row-major copies are dropped
+        head = head.packed()
+        torch.cuda.synchronize()
     h, s0, root = (torch.from_numpy(req.h).to(dev), torch.from_numpy(req.s0).to(dev),
                    torch.from_numpy(req.root_tok).to(dev))
     R, D, W, k, B = wl.R, wl.D, wl.W, wl.k, wl.B
@@ -134,7 +138,7 @@ def main():
     # the same steps again with every library launch bracketed by HIP events
     pk_ms, _ = timed_region(True)
     kern = {}
-    for name in ("gemm1", "gemm2", "head", "merge_select"):
+    for name in ("gemm1", "gemm2", "reduce", "head", "merge_select"):
         tot, n = A.timing_read(name)
         kern[name] = dict(launches=n, avg_us=(tot * 1e3 / n) if n else None)
     head_us = kern["head"]["avg_us"]

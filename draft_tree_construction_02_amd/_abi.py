@@ -17,13 +17,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdartree.so")
 
 DT_F32, DT_BF16 = 0, 1
-DT_K_GEMM1, DT_K_GEMM2, DT_K_HEAD, DT_K_MERGE = 0, 1, 2, 3
-KERNEL_CLASSES = {"gemm1": DT_K_GEMM1, "gemm2": DT_K_GEMM2, "head": DT_K_HEAD,
-                  "merge_select": DT_K_MERGE}
+DT_LAYOUT_ROWMAJOR, DT_LAYOUT_PACKED = 0, 1
+KERNEL_CLASSES = {"gemm1": 0, "gemm2": 1, "head": 2, "merge_select": 3, "reduce": 4}
 
 # every symbol include/dartree.h declares
 EXPORTS = [
-    "dartree_status_string", "dartree_version",
+    "dartree_status_string", "dartree_version", "pack_head_bytes", "pack_head",
     "build_supertree_workspace_size", "build_supertree",
     "head_step_workspace_size", "state_update", "corrected_topk",
     "prune_topB", "build_tree_mask",
@@ -40,7 +39,7 @@ class DartreeError(RuntimeError):
 
 class dt_head(C.Structure):
     _fields_ = [("d", C.c_int32), ("V", C.c_int32), ("wdtype", C.c_int32),
-                ("reserved", C.c_int32), ("E", C.c_void_p), ("W1t", C.c_void_p),
+                ("layout", C.c_int32), ("E", C.c_void_p), ("W1t", C.c_void_p),
                 ("W2t", C.c_void_p), ("Ut", C.c_void_p)]
 
 
@@ -60,6 +59,8 @@ def lib():
         sig = {
             "dartree_status_string": (C.c_char_p, [i32]),
             "dartree_version": (i32, []),
+            "pack_head_bytes": (sz, [hp]),
+            "pack_head": (i32, [hp, vp, sz, hp, vp]),
             "build_supertree_workspace_size": (sz, [hp, i32, i32, i32, i32]),
             "build_supertree": (i32, [hp, vp, vp, vp, i32, i32, i32, i32, f32,
                                       vp, vp, vp, vp, vp, sz, vp]),
@@ -142,6 +143,23 @@ class Head:
     @property
     def ref(self):
         return C.byref(self.c)
+
+    def packed(self, stream=None) -> "Head":
+        """A copy of this bf16 head with W1t, W2t and Ut in the packed block
+        layout (pack_head); the new head keeps the packed buffer alive."""
+        if self.dtype != torch.bfloat16:
+            raise ValueError("only bf16 heads are packed")
+        nbytes = int(lib().pack_head_bytes(self.ref))
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        out = dt_head()
+        _check(lib().pack_head(self.ref, _ptr(buf), nbytes, C.byref(out), _stream(stream)),
+               "pack_head")
+        h = Head.__new__(Head)
+        h.E, h.W1t, h.W2t, h.Ut = self.E, None, None, None
+        h._packed_buf = buf
+        h.V, h.d, h.dtype, h.device = self.V, self.d, self.dtype, self.device
+        h.c = out
+        return h
 
 
 def build_supertree_workspace_size(head: Head, R, D, W, k) -> int:

@@ -114,4 +114,21 @@ struct MaxSum {
   }
 };
 
+// Packed hi/lo activation planes of an [Mp][K] matrix (K % 32 == 0): block
+// (m / 16, k / 32) of 16 rows x 32 K is 512 contiguous bf16 in MFMA operand
+// order; lane l of the block holds row l % 16, K 8 (l / 16) .. + 8.
+// Writes 8 consecutive columns k .. k + 7 (k % 8 == 0) of row m.
+__device__ __forceinline__ void write_packed8(uint16_t* hi, uint16_t* lo, int K, int m, int k,
+                                              const float (&y)[8]) {
+  const int lane = (m & 15) + 16 * ((k & 31) >> 3);
+  const long off = ((long)(m >> 4) * (K >> 5) + (k >> 5)) * 512 + lane * 8;
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) split_hi_lo(y[i], h[i], l[i]);
+  *(u32x4*)(hi + off) = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                              h[6] | (h[7] << 16)};
+  *(u32x4*)(lo + off) = u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16),
+                              l[6] | (l[7] << 16)};
+}
+
 }  // namespace dt

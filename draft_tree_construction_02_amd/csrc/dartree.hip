@@ -40,12 +40,14 @@ int kmax_for(int k, bool greedy) {
   return 16;
 }
 
-// Largest divisor s of nk with tiles * s <= 768 (enough workgroups to cover
-// 256 CUs a few times without making each split trivially short).
-int choose_splits(int nk, int tiles) {
+// Split count for a split-K GEMM of K (nk chunks) over `tiles` column
+// tiles: the largest divisor s of nk with at most 640 workgroups and fp32
+// partial traffic (written and read: 8 s Mp bytes per column) at most a
+// quarter of the weight bytes (2 K per column).
+int choose_splits(int nk, int tiles, int Mp, int K) {
   int best = 1;
   for (int s = 1; s <= nk; ++s)
-    if (nk % s == 0 && (long)tiles * s <= 768) best = s;
+    if (nk % s == 0 && (long)tiles * s <= 640 && 16L * s * Mp <= K) best = s;
   return best;
 }
 
@@ -64,16 +66,19 @@ struct Carver {
 bool head_ok(const dt_head* h) {
   if (!h || !h->E || !h->W1t || !h->W2t || !h->Ut) return false;
   if (h->V < 1 || h->d < 1) return false;
+  if (h->layout != DT_LAYOUT_ROWMAJOR && h->layout != DT_LAYOUT_PACKED) return false;
   if (h->wdtype == DT_BF16) return h->d % 128 == 0;
-  if (h->wdtype == DT_F32) return h->d % 32 == 0;
+  if (h->wdtype == DT_F32) return h->d % 32 == 0 && h->layout == DT_LAYOUT_ROWMAJOR;
   return false;
 }
 
-// Layout of the state-update + head workspace for Mp rows.
+// Workspace of the state update + head for Mp rows.
 struct StepWs {
-  float* part;
-  uint32_t* counters;
-  float* H;
+  float* part;                 // split-K partials (shared by both GEMMs)
+  float* H;                    // [Mp][4d] fp32 (fp32 heads)
+  uint16_t *H_hi, *H_lo;       // [Mp][4d] packed (bf16 heads)
+  uint16_t *x_hi, *x_lo;       // [Mp][d] packed (bf16 heads)
+  uint16_t *s_hi, *s_lo;       // [Mp][d] packed (bf16 heads)
   float2* ms_part;
   uint64_t* key_part;
   int32_t* cand_tok;
@@ -82,28 +87,35 @@ struct StepWs {
   int32_t* tok[2];
   float* score[2];
   int32_t* src[2];
-  float* S[2];
-  int Mp, tiles1, tiles2, tilesV, splits1, splits2, ncounters, kt;
+  float* S[2];                 // [Mp][d] fp32 updated states (ping-pong)
+  int Mp, tiles1, tiles2, tilesV, splits1, splits2;
 };
 
-StepWs carve_step(Carver& c, const dt_head* h, int rows, int k, bool keep_states) {
+StepWs carve_step(Carver& c, const dt_head* h, int rows, int k) {
   StepWs w{};
   const int bf = h->wdtype == DT_BF16;
   const int d = h->d, V = h->V;
-  const int TN = gemm_tile_n(bf), KC = gemm_k_chunk(bf, 0);
+  const int TN = gemm_tile_n(bf), KC = gemm_k_chunk(bf);
   w.Mp = padded_rows(rows);
   w.tiles1 = (4 * d + TN - 1) / TN;
   w.tiles2 = (d + TN - 1) / TN;
   w.tilesV = (V + head_tile_n(bf) - 1) / head_tile_n(bf);
-  w.splits1 = choose_splits(d / KC, w.tiles1);
-  w.splits2 = choose_splits(4 * d / KC, w.tiles2);
-  w.ncounters = w.tiles1 > w.tiles2 ? w.tiles1 : w.tiles2;
-  w.kt = k;
+  w.splits1 = choose_splits(d / KC, w.tiles1, w.Mp, d);
+  w.splits2 = choose_splits(4 * d / KC, w.tiles2, w.Mp, 4 * d);
   const size_t part1 = (size_t)w.splits1 * w.Mp * 4 * d;
   const size_t part2 = (size_t)w.splits2 * w.Mp * d;
+  const size_t md = (size_t)w.Mp * d;
   w.part = c.take<float>(part1 > part2 ? part1 : part2);
-  w.counters = c.take<uint32_t>(w.ncounters);
-  w.H = c.take<float>((size_t)w.Mp * 4 * d);
+  if (bf) {
+    w.H_hi = c.take<uint16_t>(4 * md);
+    w.H_lo = c.take<uint16_t>(4 * md);
+    w.x_hi = c.take<uint16_t>(md);
+    w.x_lo = c.take<uint16_t>(md);
+    w.s_hi = c.take<uint16_t>(md);
+    w.s_lo = c.take<uint16_t>(md);
+  } else {
+    w.H = c.take<float>(4 * md);
+  }
   w.ms_part = c.take<float2>((size_t)w.Mp * w.tilesV);
   w.key_part = c.take<uint64_t>((size_t)w.Mp * w.tilesV * k);
   w.cand_tok = c.take<int32_t>((size_t)w.Mp * k);
@@ -113,7 +125,7 @@ StepWs carve_step(Carver& c, const dt_head* h, int rows, int k, bool keep_states
     w.tok[i] = c.take<int32_t>(w.Mp);
     w.score[i] = c.take<float>(w.Mp);
     w.src[i] = c.take<int32_t>(w.Mp);
-    w.S[i] = keep_states ? c.take<float>((size_t)w.Mp * d) : nullptr;
+    w.S[i] = c.take<float>(md);
   }
   return w;
 }
@@ -170,22 +182,26 @@ void collect_pending() {
 // ---------------------------------------------------------------- one depth
 struct DepthIo {
   const float* s_prev;      // residual source (rows indexed by src)
-  const int32_t* tok;       // tokens entering the update
+  const int32_t* tok;       // tokens entering the update (fp32 heads)
   const int32_t* src;       // residual row of each row (-1 none)
-  const float* h;           // hidden base for this depth
+  const float* h;           // hidden base for this depth (fp32 heads)
   long h_req_stride;
   int rpr;
   int rows;
-  float* s_out;             // updated states [Mp or rows][d]
+  float* s_out;             // updated states, rows_out rows of d
+  int rows_out;
 };
 
+// s' = s_parent + GELU(x W1) W2: two split-K GEMMs, each followed by its
+// in-order reduction.  bf16 heads read x from the packed planes in w.x_*.
 hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hipStream_t st) {
   const int bf = hd->wdtype == DT_BF16, d = hd->d;
+  const int packed = hd->layout == DT_LAYOUT_PACKED;
   GemmArgs g1;
+  g1.pa = PackedA{w.x_hi, w.x_lo, d};
   g1.a.gather = 1;
   g1.a.E = hd->E;
   g1.a.ldE = d;
-  g1.a.e_bf16 = bf;
   g1.a.tok = io.tok;
   g1.a.h = io.h;
   g1.a.h_req_stride = io.h_req_stride;
@@ -193,45 +209,72 @@ hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hip
   g1.a.rows = io.rows;
   g1.Wt = hd->W1t;
   g1.w_bf16 = bf;
+  g1.w_packed = packed;
   g1.N = 4 * d;
   g1.K = d;
   g1.Mp = w.Mp;
   g1.splits = w.splits1;
   g1.part = w.part;
-  g1.counters = w.counters;
-  g1.epi = EPI_GELU;
-  g1.out = w.H;
   hipError_t e = timed(DT_K_GEMM1, st, [&] { return launch_gemm(g1, st); });
+  if (e != hipSuccess) return e;
+  ReduceArgs r1;
+  r1.part = w.part;
+  r1.splits = w.splits1;
+  r1.Mp = w.Mp;
+  r1.N = 4 * d;
+  r1.rows = io.rows;
+  r1.rows_out = io.rows;
+  r1.epi = EPI_GELU;
+  r1.out = bf ? nullptr : w.H;
+  r1.out_hi = bf ? w.H_hi : nullptr;
+  r1.out_lo = bf ? w.H_lo : nullptr;
+  e = timed(DT_K_REDUCE, st, [&] { return launch_reduce(r1, st); });
   if (e != hipSuccess) return e;
 
   GemmArgs g2;
+  g2.pa = PackedA{w.H_hi, w.H_lo, 4 * d};
   g2.a.a = w.H;
   g2.a.lda = 4 * d;
   g2.a.rows = io.rows;
   g2.Wt = hd->W2t;
   g2.w_bf16 = bf;
+  g2.w_packed = packed;
   g2.N = d;
   g2.K = 4 * d;
   g2.Mp = w.Mp;
   g2.splits = w.splits2;
   g2.part = w.part;
-  g2.counters = w.counters;
-  g2.epi = EPI_RESID;
-  g2.out = io.s_out;
-  g2.s_prev = io.s_prev;
-  g2.src_row = io.src;
-  return timed(DT_K_GEMM2, st, [&] { return launch_gemm(g2, st); });
+  e = timed(DT_K_GEMM2, st, [&] { return launch_gemm(g2, st); });
+  if (e != hipSuccess) return e;
+  ReduceArgs r2;
+  r2.part = w.part;
+  r2.splits = w.splits2;
+  r2.Mp = w.Mp;
+  r2.N = d;
+  r2.rows = io.rows;
+  r2.rows_out = io.rows_out;
+  r2.epi = EPI_RESID;
+  r2.s_prev = io.s_prev;
+  r2.src_row = io.src;
+  r2.out = io.s_out;
+  r2.out_hi = bf ? w.s_hi : nullptr;
+  r2.out_lo = bf ? w.s_lo : nullptr;
+  return timed(DT_K_REDUCE, st, [&] { return launch_reduce(r2, st); });
 }
 
+// Head + merge over `rows` states; bf16 heads read s' from w.s_* (packed),
+// fp32 heads from the dense fp32 rows s.
 hipError_t run_head(const dt_head* hd, const StepWs& w, const float* s, int rows, int k, float T,
                     int32_t* cand_tok, float* cand_lp, float* lse, hipStream_t st) {
   const bool greedy = T == 0.f;
   HeadArgs p;
+  p.pa = PackedA{w.s_hi, w.s_lo, hd->d};
   p.a.a = s;
   p.a.lda = hd->d;
   p.a.rows = rows;
   p.Ut = hd->Ut;
   p.w_bf16 = hd->wdtype == DT_BF16;
+  p.w_packed = hd->layout == DT_LAYOUT_PACKED;
   p.V = hd->V;
   p.d = hd->d;
   p.Mp = w.Mp;
@@ -279,7 +322,7 @@ static int build_args_ok(const dt_head* head, int R, int D, int W, int k) {
 size_t build_supertree_workspace_size(const dt_head* head, int R, int D, int W, int k) {
   if (build_args_ok(head, R, D, W, k) != DT_OK) return 0;
   Carver c(nullptr);
-  carve_step(c, head, R * W, k, true);
+  carve_step(c, head, R * W, k);
   return c.off;
 }
 
@@ -296,12 +339,23 @@ int build_supertree(const dt_head* head, const float* h, const float* s0, const 
   if (!workspace || workspace_bytes < need) return DT_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   Carver c(workspace);
-  StepWs w = carve_step(c, head, R * W, k, true);
+  StepWs w = carve_step(c, head, R * W, k);
   const int d = head->d, rows = R * W;
   const bool greedy = T == 0.f;
+  const bool bf = head->wdtype == DT_BF16;
 
+  PrepArgs prep;
+  prep.E = (const uint16_t*)head->E;
+  prep.d = d;
+  prep.h = h;
+  prep.h_req_stride = (long)D * d;
+  prep.rpr = W;
+  prep.rows = rows;
+  prep.Mp = w.Mp;
+  prep.hi = w.x_hi;
+  prep.lo = w.x_lo;
   hipError_t e = launch_beam_init(R, W, w.Mp, root_tok, w.tok[0], w.score[0], w.src[0],
-                                  w.counters, w.ncounters, st);
+                                  bf ? &prep : nullptr, st);
   for (int t = 0; t < D && e == hipSuccess; ++t) {
     const int cur = t & 1, nxt = cur ^ 1;
     DepthIo io;
@@ -313,6 +367,7 @@ int build_supertree(const dt_head* head, const float* h, const float* s0, const 
     io.rpr = W;
     io.rows = rows;
     io.s_out = w.S[cur];
+    io.rows_out = rows;
     e = run_update(head, w, io, st);
     if (e != hipSuccess) break;
     e = run_head(head, w, w.S[cur], rows, k, T, w.cand_tok, w.cand_lp, w.lse, st);
@@ -330,6 +385,10 @@ int build_supertree(const dt_head* head, const float* h, const float* s0, const 
     b.score_out = w.score[nxt];
     b.src_out = w.src[nxt];
     b.Mp = w.Mp;
+    if (bf && t + 1 < D) {
+      b.prep = prep;
+      b.prep.h = h + (long)(t + 1) * d;
+    }
     e = timed(DT_K_MERGE, st, [&] { return launch_beam_select(b, st); });
   }
   return e == hipSuccess ? DT_OK : DT_EHIP;
@@ -340,7 +399,7 @@ size_t head_step_workspace_size(const dt_head* head, int rows, int k) {
       k > head->V)
     return 0;
   Carver c(nullptr);
-  carve_step(c, head, rows, k, false);
+  carve_step(c, head, rows, k);
   return c.off;
 }
 
@@ -354,8 +413,22 @@ int state_update(const dt_head* head, const float* s_in, const int32_t* tok, con
   if (!workspace || workspace_bytes < need) return DT_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   Carver c(workspace);
-  StepWs w = carve_step(c, head, rows, 1, false);
-  hipError_t e = launch_fill_rows(rows, w.Mp, tok, w.tok[0], w.src[0], w.counters, w.ncounters, st);
+  StepWs w = carve_step(c, head, rows, 1);
+  hipError_t e = launch_fill_rows(rows, w.Mp, tok, w.tok[0], w.src[0], st);
+  if (e == hipSuccess && head->wdtype == DT_BF16) {
+    PrepArgs prep;
+    prep.E = (const uint16_t*)head->E;
+    prep.d = head->d;
+    prep.tok = w.tok[0];
+    prep.h = h;
+    prep.h_req_stride = 0;
+    prep.rpr = 1;
+    prep.rows = rows;
+    prep.Mp = w.Mp;
+    prep.hi = w.x_hi;
+    prep.lo = w.x_lo;
+    e = launch_prep_x(prep, st);
+  }
   if (e == hipSuccess) {
     DepthIo io;
     io.s_prev = s_in;
@@ -366,6 +439,7 @@ int state_update(const dt_head* head, const float* s_in, const int32_t* tok, con
     io.rpr = 1;
     io.rows = rows;
     io.s_out = s_out;
+    io.rows_out = rows;
     e = run_update(head, w, io, st);
   }
   return e == hipSuccess ? DT_OK : DT_EHIP;
@@ -382,9 +456,54 @@ int corrected_topk(const dt_head* head, const float* s, int rows, int k, float T
   if (!workspace || workspace_bytes < need) return DT_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   Carver c(workspace);
-  StepWs w = carve_step(c, head, rows, k, false);
-  hipError_t e = run_head(head, w, s, rows, k, T, cand_tok, cand_lp, lse, st);
+  StepWs w = carve_step(c, head, rows, k);
+  hipError_t e = hipSuccess;
+  if (head->wdtype == DT_BF16) {
+    // split the caller's fp32 states into the packed hi/lo planes
+    ReduceArgs r;
+    r.part = s;
+    r.splits = 1;
+    r.Mp = w.Mp;
+    r.N = head->d;
+    r.rows = rows;
+    r.rows_out = 0;
+    r.epi = EPI_RESID;
+    r.out_hi = w.s_hi;
+    r.out_lo = w.s_lo;
+    e = launch_reduce(r, st);
+  }
+  if (e == hipSuccess) e = run_head(head, w, s, rows, k, T, cand_tok, cand_lp, lse, st);
   return e == hipSuccess ? DT_OK : DT_EHIP;
+}
+
+size_t pack_head_bytes(const dt_head* head) {
+  if (!head_ok(head) || head->wdtype != DT_BF16) return 0;
+  const size_t d = head->d, V = head->V;
+  const size_t vpad = (V + 15) / 16 * 16;
+  return align_up(4 * d * d * 2) * 2 + align_up(vpad * d * 2);
+}
+
+int pack_head(const dt_head* src, void* dst, size_t dst_bytes, dt_head* packed, void* stream) {
+  if (!head_ok(src) || !packed) return DT_EINVAL;
+  if (src->wdtype != DT_BF16 || src->layout != DT_LAYOUT_ROWMAJOR) return DT_EINVAL;
+  const size_t need = pack_head_bytes(src);
+  if (!dst || dst_bytes < need) return DT_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int d = src->d;
+  char* base = (char*)dst;
+  uint16_t* w1 = (uint16_t*)base;
+  uint16_t* w2 = (uint16_t*)(base + align_up((size_t)4 * d * d * 2));
+  uint16_t* u = (uint16_t*)(base + 2 * align_up((size_t)4 * d * d * 2));
+  hipError_t e = launch_pack_weight((const uint16_t*)src->W1t, w1, 4 * d, d, st);
+  if (e == hipSuccess) e = launch_pack_weight((const uint16_t*)src->W2t, w2, d, 4 * d, st);
+  if (e == hipSuccess) e = launch_pack_weight((const uint16_t*)src->Ut, u, src->V, d, st);
+  if (e != hipSuccess) return DT_EHIP;
+  *packed = *src;
+  packed->layout = DT_LAYOUT_PACKED;
+  packed->W1t = w1;
+  packed->W2t = w2;
+  packed->Ut = u;
+  return DT_OK;
 }
 
 int prune_topB(const float* pool_score, const int32_t* pool_parent, const int32_t* n_valid, int R,

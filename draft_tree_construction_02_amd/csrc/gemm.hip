@@ -2,22 +2,28 @@
 //
 // Every product here has the shape Y[M][N] = A[M][K] * Wt[N][K]^T with a few
 // dozen rows M (the surviving branches), and N, K in the thousands: the time
-// is the weight stream from HBM, read exactly once per call.  A workgroup
-// (4 waves) owns a 128-column tile of Wt (one contiguous block of rows of the
-// output-feature-major weight) and a K range; each wave streams its own 32
-// weight rows with non-temporal 16-byte loads, one K iteration ahead of the
-// MFMAs that consume them.
+// is the weight stream from HBM, read exactly once per call.
 //
-// bf16 weights: the fp32 activations are split into hi = bf16(a) and
-// lo = bf16(a - hi) while being staged into LDS, and both halves go through
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation, which carries ~16
-// significant bits of A (bf16 weights are exact).  fp32 weights use plain FMA.
+// bf16 path.  Weights are streamed in the packed block layout (1 KB blocks of
+// 16 rows x 32 K in MFMA operand order, see pack.hip) with non-temporal
+// 16-byte loads, so every wave load instruction reads one contiguous 1 KB
+// block; row-major weights are also accepted (16 rows x 64 B per
+// instruction).  Activations arrive as packed hi/lo bf16 planes (hi = bf16(a),
+// lo = bf16(a - hi)), written by the producing kernel; both halves go through
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation, carrying ~16 significant
+// bits of A (bf16 weights are exact).  A workgroup (4 waves) owns 128 output
+// columns; each wave streams its own 2 x 16 weight rows one 128-K iteration
+// ahead of the MFMAs, while the activation chunk is staged in LDS and shared
+// by the 4 waves.
+//
+// fp32 path (fp32 heads): plain FMA with fp32 activations staged in LDS.
 //
 // The head GEMM (z = s' U) never writes logits to HBM: each workgroup leaves
 // its logit tile in LDS and reduces it per row to (max, sum exp) and the
-// tile's top-k keys.  The state-update GEMMs use split-K; the last split to
-// finish a column tile sums all splits in order and applies the epilogue
-// (GELU, or residual add of the parent's state), so results are deterministic.
+// tile's top-k keys.  The state-update GEMMs are split-K; each split writes
+// its fp32 partial and a separate reduce kernel sums the splits in order and
+// applies the epilogue (the kernel boundary makes the partials visible
+// without a device-wide cache flush per workgroup).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -31,122 +37,79 @@ constexpr int TN_F = 64;              // columns per fp32 workgroup
 constexpr int KC_B = 128;             // K staged per LDS chunk (bf16 path)
 constexpr int KC_F = 32;              // K staged per LDS chunk (fp32 path)
 constexpr int CPAD = 4;               // C tile row padding (floats)
+constexpr int BLK = 512;              // bf16 elements per packed block (1 KB)
 
 int gemm_tile_n(int w_bf16) { return w_bf16 ? TN_B : TN_F; }
 int head_tile_n(int w_bf16) { return w_bf16 ? TN_B : TN_F; }
-int gemm_k_chunk(int w_bf16, int) { return w_bf16 ? KC_B : KC_F; }
+int gemm_k_chunk(int w_bf16) { return w_bf16 ? KC_B : KC_F; }
 
 __device__ __forceinline__ float gelu_f(float y) {
   return 0.5f * y * (1.0f + erff(y * 0.70710678118654752f));
 }
 
 // ----------------------------------------------------------------------------
-// A staging: fp32 activations (dense rows, or gathered embedding + hidden)
+// bf16 path: packed hi/lo activation chunk -> LDS
 // ----------------------------------------------------------------------------
-template <int Mp, int KC, bool GATHER, bool EBF16>
-struct AStage {
-  static constexpr int KQ = KC / 4;                       // float4 groups per row
-  static constexpr int NG = Mp * KQ;                      // groups per chunk
-  static constexpr int NA = (NG + NT - 1) / NT;           // groups per thread
-  float4 a[NA];
-  float4 hv[NA];
-  uint2 eb[NA];
+// LDS chunk layout: [hl][mt][kb][512] with kb the 32-wide K block inside the
+// chunk; every block is copied whole (64 lanes x 16 B).
+template <int MT, int KC>
+struct AStagePacked {
+  static constexpr int KB = KC / 32;                  // blocks per row tile
+  static constexpr int NBLK = 2 * MT * KB;            // blocks per chunk
+  static constexpr int PER_WAVE = NBLK / NWAVES;      // blocks per wave
+  static_assert(NBLK % NWAVES == 0, "chunk must split over waves");
+  u32x4 v[PER_WAVE];
 
-  __device__ __forceinline__ void issue(const ASrc& s, int k) {
-    const int tid = threadIdx.x;
+  __device__ __forceinline__ void issue(const PackedA& a, int k) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kblocks = a.K / 32;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int g = tid + i * NT;
-      const int m = g / KQ, kk = k + (g % KQ) * 4;
-      a[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      hv[i] = a[i];
-      eb[i] = make_uint2(0u, 0u);
-      if (g < NG && m < s.rows) {
-        if (GATHER) {
-          const int t = s.tok[m];
-          if (t >= 0) {
-            hv[i] = *(const float4*)(s.h + (long)(m / s.rpr) * s.h_req_stride + kk);
-            if (EBF16)
-              eb[i] = *(const uint2*)((const uint16_t*)s.E + (long)t * s.ldE + kk);
-            else
-              a[i] = *(const float4*)((const float*)s.E + (long)t * s.ldE + kk);
-          }
-        } else {
-          a[i] = *(const float4*)(s.a + (long)m * s.lda + kk);
-        }
-      }
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int bi = wave + i * NWAVES;
+      const int hl = bi / (MT * KB), rem = bi % (MT * KB), mt = rem / KB, kb = rem % KB;
+      const uint16_t* src = (hl ? a.lo : a.hi) + ((long)mt * kblocks + k / 32 + kb) * BLK;
+      v[i] = *(const u32x4*)(src + lane * 8);
     }
   }
-
-  __device__ __forceinline__ float4 value(int i) const {
-    if (!GATHER) return a[i];
-    float4 e = a[i];
-    if (EBF16) {
-      e.x = bf16_to_f32(eb[i].x & 0xffffu);
-      e.y = bf16_to_f32(eb[i].x >> 16);
-      e.z = bf16_to_f32(eb[i].y & 0xffffu);
-      e.w = bf16_to_f32(eb[i].y >> 16);
-    }
-    return make_float4(e.x + hv[i].x, e.y + hv[i].y, e.z + hv[i].z, e.w + hv[i].w);
-  }
-
-  // bf16 path: hi plane at As, lo plane at As + Mp * LDA.
-  __device__ __forceinline__ void commit_split(uint16_t* As) const {
-    constexpr int LDA = KC + 8;
-    const int tid = threadIdx.x;
+  __device__ __forceinline__ void commit(uint16_t* As) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int g = tid + i * NT;
-      if (g < NG) {
-        const int m = g / KQ, kk = (g % KQ) * 4;
-        const float4 x = value(i);
-        uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-        split_hi_lo(x.x, h0, l0);
-        split_hi_lo(x.y, h1, l1);
-        split_hi_lo(x.z, h2, l2);
-        split_hi_lo(x.w, h3, l3);
-        *(uint2*)(As + m * LDA + kk) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-        *(uint2*)(As + Mp * LDA + m * LDA + kk) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
-      }
-    }
-  }
-
-  // fp32 path
-  __device__ __forceinline__ void commit_f32(float* As) const {
-    constexpr int LDA = KC + 4;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int g = tid + i * NT;
-      if (g < NG) {
-        const int m = g / KQ, kk = (g % KQ) * 4;
-        *(float4*)(As + m * LDA + kk) = value(i);
-      }
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int bi = wave + i * NWAVES;
+      *(u32x4*)(As + bi * BLK + lane * 8) = v[i];
     }
   }
 };
 
-// ----------------------------------------------------------------------------
-// bf16 MFMA mainloop
-// ----------------------------------------------------------------------------
-// Lane (r = lane % 16, g = lane / 16) of a wave loads 32 consecutive K values
-// (64 bytes) of weight row n = col0 + 16 c + r per 128-K iteration; MFMA j of
-// the iteration uses elements [8 j, 8 j + 8) of that run, and the activation
-// fragment uses the same K positions, so the product sums every K once.
-template <int MT>
+// Weight fragments of one 128-K iteration: b[c][j] is the 16 x 32 block of
+// column tile c and K step j, in MFMA operand order (lane l: row l % 16,
+// K 8 (l / 16) .. + 8 of the step).
+template <bool PACKED>
 __device__ __forceinline__ void load_b(u32x4 (&b)[NW][4], const uint16_t* __restrict__ Wt,
-                                       int ldw, int col0, int N, int kb, int lane) {
-  const int r = lane & 15, g = lane >> 4;
+                                       int K, int col0, int N, int kb, int lane) {
 #pragma unroll
   for (int c = 0; c < NW; ++c) {
-    const int n = col0 + 16 * c + r;
-    if (n < N) {
-      const u32x4* p = (const u32x4*)(Wt + (long)n * ldw + kb + g * 32);
+    const int nt = col0 + 16 * c;            // first row of this column tile
+    if (PACKED) {
+      if (nt < N) {
+        const u32x4* p = (const u32x4*)(Wt + ((long)(nt / 16) * (K / 32) + kb / 32) * BLK +
+                                        lane * 8);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) b[c][q] = __builtin_nontemporal_load(p + q);
+        for (int j = 0; j < 4; ++j) b[c][j] = __builtin_nontemporal_load(p + j * (BLK / 8));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[c][j] = u32x4{0u, 0u, 0u, 0u};
+      }
     } else {
+      const int n = nt + (lane & 15);
+      if (n < N) {
+        const uint16_t* p = Wt + (long)n * K + kb + (lane >> 4) * 8;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) b[c][q] = u32x4{0u, 0u, 0u, 0u};
+        for (int j = 0; j < 4; ++j) b[c][j] = *(const u32x4*)(p + 32 * j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[c][j] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   }
 }
@@ -154,16 +117,15 @@ __device__ __forceinline__ void load_b(u32x4 (&b)[NW][4], const uint16_t* __rest
 template <int MT, int KC>
 __device__ __forceinline__ void mma_iter(const uint16_t* As, int it, const u32x4 (&b)[NW][4],
                                          f32x4 (&acc)[NW][MT], int lane) {
-  constexpr int Mp = 16 * MT;
-  constexpr int LDA = KC + 8;
-  const int r = lane & 15, g = lane >> 4;
+  constexpr int KB = KC / 32;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const uint16_t* p = As + (16 * mt + r) * LDA + it * 128 + g * 32 + j * 8;
-      const bf16x8 ahi = __builtin_bit_cast(bf16x8, *(const u32x4*)p);
-      const bf16x8 alo = __builtin_bit_cast(bf16x8, *(const u32x4*)(p + Mp * LDA));
+      const int blk = mt * KB + it * 4 + j;
+      const bf16x8 ahi = __builtin_bit_cast(bf16x8, *(const u32x4*)(As + blk * BLK + lane * 8));
+      const bf16x8 alo = __builtin_bit_cast(
+          bf16x8, *(const u32x4*)(As + (MT * KB + blk) * BLK + lane * 8));
 #pragma unroll
       for (int c = 0; c < NW; ++c)
         acc[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -180,46 +142,45 @@ template <int MT, int NBUF>
 struct BfCfg {
   static constexpr int Mp = 16 * MT;
   static constexpr int KC = KC_B;
-  static constexpr int LDA = KC + 8;
-  static constexpr int ABUF = 2 * Mp * LDA;                 // uint16 per buffer
+  static constexpr int ABUF = 2 * MT * (KC / 32) * BLK;     // bf16 per buffer
   static constexpr int A_BYTES = NBUF * ABUF * 2;
   static constexpr int C_BYTES = Mp * (TN_B + CPAD) * 4;
   static constexpr int LDS = A_BYTES > C_BYTES ? A_BYTES : C_BYTES;
 };
 
-// Accumulates Y[0..Mp)[n0..n0+128) over K range [k0, k0 + klen) and leaves it
-// in the LDS C tile (row stride TN_B + CPAD floats), scaled by `scale`.
-template <int MT, int NBUF, bool GATHER>
-__device__ __forceinline__ void tile_bf16(const ASrc& src, const uint16_t* __restrict__ Wt,
-                                          int K, int N, int n0, int k0, int klen, float scale,
-                                          unsigned char* smem) {
+// Accumulates Y[0..Mp)[n0..n0+128) over K range [k0, k0 + klen).  On return
+// acc[c][mt] holds rows 16 mt + lane % 16, columns n0 + 32 wave + 16 c +
+// 4 (lane / 16) + i (i = 0..3) in element i.
+template <int MT, int NBUF, bool PW>
+__device__ __forceinline__ void tile_bf16(const PackedA& a, const uint16_t* __restrict__ Wt,
+                                          int N, int n0, int k0, int klen, unsigned char* smem,
+                                          f32x4 (&acc)[NW][MT]) {
   using C = BfCfg<MT, NBUF>;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   uint16_t* As = (uint16_t*)smem;
-  f32x4 acc[NW][MT];
 #pragma unroll
   for (int c = 0; c < NW; ++c)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  AStage<C::Mp, C::KC, GATHER, true> st;
-  st.issue(src, k0);
-  st.commit_split(As);
+  AStagePacked<MT, C::KC> st;
+  const int col0 = n0 + wave * NW * 16;
+  u32x4 bc[NW][4], bn[NW][4];
+  load_b<PW>(bc, Wt, a.K, col0, N, k0, lane);
+  st.issue(a, k0);
+  st.commit(As);
   __syncthreads();
 
-  const int col0 = n0 + wave * NW * 16;
   const int nst = klen / C::KC;
-  u32x4 bc[NW][4], bn[NW][4];
-  load_b<MT>(bc, Wt, K, col0, N, k0, lane);
   for (int s = 0; s < nst; ++s) {
     const uint16_t* Ab = As + (NBUF == 2 ? (s & 1) * C::ABUF : 0);
     const bool more = s + 1 < nst;
-    if (more) st.issue(src, k0 + (s + 1) * C::KC);
-    if (more) load_b<MT>(bn, Wt, K, col0, N, k0 + (s + 1) * C::KC, lane);
+    if (more) load_b<PW>(bn, Wt, a.K, col0, N, k0 + (s + 1) * C::KC, lane);
+    if (more) st.issue(a, k0 + (s + 1) * C::KC);
     mma_iter<MT, C::KC>(Ab, 0, bc, acc, lane);
     if (more) {
       if (NBUF == 1) __syncthreads();
-      st.commit_split(As + (NBUF == 2 ? ((s + 1) & 1) * C::ABUF : 0));
+      st.commit(As + (NBUF == 2 ? ((s + 1) & 1) * C::ABUF : 0));
 #pragma unroll
       for (int c = 0; c < NW; ++c)
 #pragma unroll
@@ -227,26 +188,51 @@ __device__ __forceinline__ void tile_bf16(const ASrc& src, const uint16_t* __res
     }
     __syncthreads();
   }
-
-  // accumulators -> LDS C tile; lane holds rows 16 mt + r, columns 4 g .. 4 g + 3
-  float* Cs = (float*)smem;
-  const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int c = 0; c < NW; ++c)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = 16 * mt + r;
-      const int n = wave * NW * 16 + c * 16 + 4 * g;
-      f32x4 v = acc[c][mt];
-      *(float4*)(Cs + m * (TN_B + CPAD) + n) =
-          make_float4(v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale);
-    }
-  __syncthreads();
 }
 
 // ----------------------------------------------------------------------------
-// fp32 FMA mainloop (fp32 heads)
+// fp32 path
 // ----------------------------------------------------------------------------
+// A row m, columns k..k+3: dense rows or gathered embedding + hidden.
+template <int Mp, int KC, bool GATHER>
+struct AStageF32 {
+  static constexpr int KQ = KC / 4;
+  static constexpr int NG = Mp * KQ;
+  static constexpr int NA = (NG + NT - 1) / NT;
+  float4 a[NA];
+
+  __device__ __forceinline__ void load(const ASrc& s, int k) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int g = tid + i * NT;
+      const int m = g / KQ, kk = k + (g % KQ) * 4;
+      a[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (g < NG && m < s.rows) {
+        if (GATHER) {
+          const int t = s.tok[m];
+          if (t >= 0) {
+            const float4 h = *(const float4*)(s.h + (long)(m / s.rpr) * s.h_req_stride + kk);
+            const float4 e = *(const float4*)((const float*)s.E + (long)t * s.ldE + kk);
+            a[i] = make_float4(e.x + h.x, e.y + h.y, e.z + h.z, e.w + h.w);
+          }
+        } else {
+          a[i] = *(const float4*)(s.a + (long)m * s.lda + kk);
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void commit(float* As) const {
+    constexpr int LDA = KC + 4;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int g = tid + i * NT;
+      if (g < NG) *(float4*)(As + (g / KQ) * LDA + (g % KQ) * 4) = a[i];
+    }
+  }
+};
+
 template <int MT>
 struct F32Cfg {
   static constexpr int Mp = 16 * MT;
@@ -257,10 +243,11 @@ struct F32Cfg {
   static constexpr int LDS = A_BYTES + C_BYTES;
 };
 
+// Leaves Y (times `scale`) in the LDS C tile [Mp][TN_F + CPAD].
 template <int MT, bool GATHER>
-__device__ __forceinline__ void tile_f32(const ASrc& src, const float* __restrict__ Wt, int K,
-                                         int N, int n0, int k0, int klen, float scale,
-                                         unsigned char* smem, float*& Cs_out) {
+__device__ __forceinline__ float* tile_f32(const ASrc& src, const float* __restrict__ Wt, int K,
+                                           int N, int n0, int k0, int klen, float scale,
+                                           unsigned char* smem) {
   using C = F32Cfg<MT>;
   constexpr int RPT = C::Mp / 4;        // rows per thread
   const int tid = threadIdx.x, nl = tid % TN_F, mg = tid / TN_F;
@@ -270,11 +257,11 @@ __device__ __forceinline__ void tile_f32(const ASrc& src, const float* __restric
 #pragma unroll
   for (int i = 0; i < RPT; ++i) acc[i] = 0.f;
   const int n = n0 + nl;
-  AStage<C::Mp, C::KC, GATHER, false> st;
+  AStageF32<C::Mp, C::KC, GATHER> st;
   for (int s = 0; s < klen / C::KC; ++s) {
     const int kb = k0 + s * C::KC;
-    st.issue(src, kb);
-    st.commit_f32(As);
+    st.load(src, kb);
+    st.commit(As);
     __syncthreads();
     if (n < N) {
 #pragma unroll
@@ -295,65 +282,95 @@ __device__ __forceinline__ void tile_f32(const ASrc& src, const float* __restric
 #pragma unroll
   for (int i = 0; i < RPT; ++i) Cs[(mg + 4 * i) * (TN_F + CPAD) + nl] = acc[i] * scale;
   __syncthreads();
-  Cs_out = Cs;
+  return Cs;
 }
 
 // ----------------------------------------------------------------------------
-// split-K state-update GEMM with fused last-split epilogue
+// split-K partial products
 // ----------------------------------------------------------------------------
-template <int MT, int TN>
-__device__ __forceinline__ void splitk_epilogue(const GemmArgs& g, const float* Cs, int tile) {
-  constexpr int Mp = 16 * MT;
-  const int tid = threadIdx.x;
-  const int n0 = tile * TN, split = blockIdx.y;
-  const int nvalid = min(TN, g.N - n0);
-  for (int idx = tid; idx < Mp * TN; idx += NT) {
-    const int m = idx / TN, n = idx % TN;
-    if (n < nvalid) g.part[((long)split * Mp + m) * g.N + n0 + n] = Cs[m * (TN + CPAD) + n];
-  }
-  __threadfence();
-  __syncthreads();
-  __shared__ int last;
-  if (tid == 0) last = atomicAdd(&g.counters[tile], 1u) == (uint32_t)(g.splits - 1);
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  const int rows = g.a.rows;
-  for (int idx = tid; idx < Mp * TN; idx += NT) {
-    const int m = idx / TN, n = idx % TN;
-    if (n >= nvalid || m >= rows) continue;
-    float y = 0.f;
-    for (int s = 0; s < g.splits; ++s) y += g.part[((long)s * Mp + m) * g.N + n0 + n];
-    float o;
-    if (g.epi == EPI_GELU) {
-      o = gelu_f(y);
-    } else {
-      const int sr = g.src_row[m];
-      o = (sr >= 0 ? g.s_prev[(long)sr * g.N + n0 + n] : 0.f) + y;
-    }
-    g.out[(long)m * g.N + n0 + n] = o;
-  }
-  if (tid == 0) g.counters[tile] = 0u;
-}
-
-template <int MT, int NBUF, bool GATHER>
+template <int MT, int NBUF, bool PW>
 __global__ __launch_bounds__(NT) void k_gemm_bf16(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[BfCfg<MT, NBUF>::LDS];
-  const int tile = blockIdx.x;
-  const int klen = g.K / g.splits, k0 = blockIdx.y * klen;
-  tile_bf16<MT, NBUF, GATHER>(g.a, (const uint16_t*)g.Wt, g.K, g.N, tile * TN_B, k0, klen, 1.f,
-                              smem);
-  splitk_epilogue<MT, TN_B>(g, (const float*)smem, tile);
+  constexpr int Mp = 16 * MT;
+  const int tile = blockIdx.x, split = blockIdx.y;
+  const int klen = g.pa.K / g.splits, k0 = split * klen;
+  const int n0 = tile * TN_B;
+  f32x4 acc[NW][MT];
+  tile_bf16<MT, NBUF, PW>(g.pa, (const uint16_t*)g.Wt, g.N, n0, k0, klen, smem, acc);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int c = 0; c < NW; ++c) {
+    const int n = n0 + wave * NW * 16 + c * 16 + 4 * q;
+    if (n >= g.N) continue;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = 16 * mt + r;
+      const f32x4 v = acc[c][mt];
+      *(float4*)(g.part + ((long)split * Mp + m) * g.N + n) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
 }
 
 template <int MT, bool GATHER>
 __global__ __launch_bounds__(NT) void k_gemm_f32(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[F32Cfg<MT>::LDS];
-  const int tile = blockIdx.x;
-  const int klen = g.K / g.splits, k0 = blockIdx.y * klen;
-  float* Cs;
-  tile_f32<MT, GATHER>(g.a, (const float*)g.Wt, g.K, g.N, tile * TN_F, k0, klen, 1.f, smem, Cs);
-  splitk_epilogue<MT, TN_F>(g, Cs, tile);
+  constexpr int Mp = 16 * MT;
+  const int tile = blockIdx.x, split = blockIdx.y;
+  const int klen = g.K / g.splits, k0 = split * klen;
+  const int n0 = tile * TN_F;
+  const float* Cs = tile_f32<MT, GATHER>(g.a, (const float*)g.Wt, g.K, g.N, n0, k0, klen, 1.f,
+                                         smem);
+  const int nvalid = min(TN_F, g.N - n0);
+  for (int idx = threadIdx.x; idx < Mp * TN_F; idx += NT) {
+    const int m = idx / TN_F, n = idx % TN_F;
+    if (n < nvalid) g.part[((long)split * Mp + m) * g.N + n0 + n] = Cs[m * (TN_F + CPAD) + n];
+  }
+}
+
+// ----------------------------------------------------------------------------
+// split-K reduction + epilogue; writes fp32 rows and (bf16 path) packed hi/lo
+// ----------------------------------------------------------------------------
+// One thread per (row m < Mp, 8 consecutive columns).  Rows >= rows are zero.
+__global__ __launch_bounds__(256) void k_reduce(ReduceArgs r) {
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int n8 = r.N / 8;
+  if (gid >= (long)r.Mp * n8) return;
+  const int m = gid / n8, n = (gid % n8) * 8;
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = 0.f;
+  if (m < r.rows) {
+    for (int s = 0; s < r.splits; ++s) {
+      const float* p = r.part + ((long)s * r.Mp + m) * r.N + n;
+      const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+      y[0] += a.x; y[1] += a.y; y[2] += a.z; y[3] += a.w;
+      y[4] += b.x; y[5] += b.y; y[6] += b.z; y[7] += b.w;
+    }
+    if (r.epi == EPI_GELU) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = gelu_f(y[i]);
+    } else {
+      const int sr = r.src_row ? r.src_row[m] : -1;
+      if (sr >= 0) {
+        const float* sp = r.s_prev + (long)sr * r.N + n;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = sp[i] + y[i];
+      }
+    }
+  }
+  if (r.out && m < r.rows_out) {
+    float* o = r.out + (long)m * r.N + n;
+    *(float4*)o = make_float4(y[0], y[1], y[2], y[3]);
+    *(float4*)(o + 4) = make_float4(y[4], y[5], y[6], y[7]);
+  }
+  if (r.out_hi) write_packed8(r.out_hi, r.out_lo, r.N, m, n, y);
+}
+
+hipError_t launch_reduce(const ReduceArgs& r, hipStream_t st) {
+  const long n = (long)r.Mp * (r.N / 8);
+  hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, r);
+  return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------
@@ -394,22 +411,35 @@ __device__ __forceinline__ void head_epilogue(const HeadArgs& p, const float* Cs
   }
 }
 
-template <int MT, int NBUF, int KMAX>
+template <int MT, int NBUF, int KMAX, bool PW>
 __global__ __launch_bounds__(NT) void k_head_bf16(HeadArgs p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[BfCfg<MT, NBUF>::LDS];
-  const int tile = blockIdx.x;
-  tile_bf16<MT, NBUF, false>(p.a, (const uint16_t*)p.Ut, p.d, p.V, tile * TN_B, 0, p.d,
-                             p.greedy ? 1.f : p.inv_T, smem);
-  head_epilogue<MT, KMAX, TN_B>(p, (const float*)smem, tile);
+  const int tile = blockIdx.x, n0 = tile * TN_B;
+  f32x4 acc[NW][MT];
+  tile_bf16<MT, NBUF, PW>(p.pa, (const uint16_t*)p.Ut, p.V, n0, 0, p.d, smem, acc);
+  // accumulators -> LDS C tile (the A buffers are free after the last barrier)
+  float* Cs = (float*)smem;
+  const float scale = p.greedy ? 1.f : p.inv_T;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int c = 0; c < NW; ++c)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const f32x4 v = acc[c][mt];
+      *(float4*)(Cs + (16 * mt + r) * (TN_B + CPAD) + wave * NW * 16 + c * 16 + 4 * q) =
+          make_float4(v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale);
+    }
+  __syncthreads();
+  head_epilogue<MT, KMAX, TN_B>(p, Cs, tile);
 }
 
 template <int MT, int KMAX>
 __global__ __launch_bounds__(NT) void k_head_f32(HeadArgs p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[F32Cfg<MT>::LDS];
   const int tile = blockIdx.x;
-  float* Cs;
-  tile_f32<MT, false>(p.a, (const float*)p.Ut, p.d, p.V, tile * TN_F, 0, p.d,
-                      p.greedy ? 1.f : p.inv_T, smem, Cs);
+  const float* Cs = tile_f32<MT, false>(p.a, (const float*)p.Ut, p.d, p.V, tile * TN_F, 0, p.d,
+                                        p.greedy ? 1.f : p.inv_T, smem);
   head_epilogue<MT, KMAX, TN_F>(p, Cs, tile);
 }
 
@@ -422,7 +452,7 @@ static hipError_t gemm_mt(const GemmArgs& g, hipStream_t st) {
   dim3 grid((g.N + TN - 1) / TN, g.splits);
   if (g.w_bf16) {
     constexpr int NB = MT >= 8 ? 1 : 2;
-    if (g.a.gather)
+    if (g.w_packed)
       hipLaunchKernelGGL((k_gemm_bf16<MT, NB, true>), grid, dim3(NT), 0, st, g);
     else
       hipLaunchKernelGGL((k_gemm_bf16<MT, NB, false>), grid, dim3(NT), 0, st, g);
@@ -451,7 +481,10 @@ static hipError_t head_mk(const HeadArgs& p, hipStream_t st) {
   dim3 grid((p.V + TN - 1) / TN);
   if (p.w_bf16) {
     constexpr int NB = MT >= 8 ? 1 : 2;
-    hipLaunchKernelGGL((k_head_bf16<MT, NB, KMAX>), grid, dim3(NT), 0, st, p);
+    if (p.w_packed)
+      hipLaunchKernelGGL((k_head_bf16<MT, NB, KMAX, true>), grid, dim3(NT), 0, st, p);
+    else
+      hipLaunchKernelGGL((k_head_bf16<MT, NB, KMAX, false>), grid, dim3(NT), 0, st, p);
   } else {
     hipLaunchKernelGGL((k_head_f32<MT, KMAX>), grid, dim3(NT), 0, st, p);
   }

@@ -3,9 +3,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.hpp"
+
 namespace dt {
 
-// Activation source of a skinny GEMM: row m, column k of the fp32 matrix A.
+// fp32 activation source (fp32 heads): row m, column k of A.
 //   dense:  A[m][k] = a[m * lda + k]
 //   gather: A[m][k] = E[tok[m]][k] + h[(m / rpr) * h_req_stride + k]
 // Rows with m >= rows, or with tok[m] < 0 in gather mode, read as zero.
@@ -14,7 +16,6 @@ struct ASrc {
   int lda = 0;
   const void* E = nullptr;
   int ldE = 0;
-  int e_bf16 = 0;
   const int32_t* tok = nullptr;
   const float* h = nullptr;
   long h_req_stride = 0;
@@ -23,38 +24,59 @@ struct ASrc {
   int rows = 0;
 };
 
-enum Epi { EPI_GELU = 0, EPI_RESID = 1 };
-
-// Split-K skinny GEMM Y = A Wt^T (Wt [N][K]) with a fused epilogue run by the
-// last split to finish each column tile, summing the splits in order:
-//   EPI_GELU : out[m][n] = GELU(Y[m][n])
-//   EPI_RESID: out[m][n] = (src_row[m] >= 0 ? s_prev[src_row[m]][n] : 0) + Y[m][n]
-struct GemmArgs {
-  ASrc a;
-  const void* Wt = nullptr;
-  int w_bf16 = 1;
-  int N = 0, K = 0;
-  int Mp = 0;                 // padded rows (16, 32, 64, 128 or 256)
-  int splits = 1;
-  float* part = nullptr;      // [splits][Mp][N]
-  uint32_t* counters = nullptr;  // [ceil(N / TN)] zero on entry, zero on exit
-  int epi = EPI_GELU;
-  float* out = nullptr;       // [Mp][N]
-  const float* s_prev = nullptr;
-  const int32_t* src_row = nullptr;
+// bf16 activation A [Mp][K] as packed hi/lo planes (see write_packed8):
+// 1 KB block (mt, kb) of 16 rows x 32 K at element offset (mt * K/32 + kb) * 512,
+// lane l of the block holding row 16 mt + l % 16, K 32 kb + 8 (l / 16) .. + 8.
+struct PackedA {
+  const uint16_t* hi = nullptr;
+  const uint16_t* lo = nullptr;
+  int K = 0;
 };
 
-// Column-tile width and K-chunk of a GEMM configuration.
+enum Epi { EPI_GELU = 0, EPI_RESID = 1 };
+
+// Split-K partial products part[split][Mp][N] of Y = A Wt^T, Wt [N][K].
+struct GemmArgs {
+  PackedA pa;                 // bf16 path
+  ASrc a;                     // fp32 path
+  const void* Wt = nullptr;
+  int w_bf16 = 1;
+  int w_packed = 0;           // bf16 weights in the packed block layout
+  int N = 0, K = 0;
+  int Mp = 0;                 // padded rows (16, 32, 64 or 128)
+  int splits = 1;
+  float* part = nullptr;
+};
+
+// Sum of the splits in order plus the epilogue:
+//   EPI_GELU : y = GELU(sum)
+//   EPI_RESID: y = (src_row[m] >= 0 ? s_prev[src_row[m]][n] : 0) + sum
+// Writes out [rows_out][N] fp32 (if out) and the packed hi/lo planes
+// [Mp][N] (if out_hi); rows >= rows are zero.
+struct ReduceArgs {
+  const float* part = nullptr;
+  int splits = 1, Mp = 0, N = 0, rows = 0, rows_out = 0;
+  int epi = EPI_GELU;
+  const float* s_prev = nullptr;
+  const int32_t* src_row = nullptr;
+  float* out = nullptr;
+  uint16_t* out_hi = nullptr;
+  uint16_t* out_lo = nullptr;
+};
+
 int gemm_tile_n(int w_bf16);
-int gemm_k_chunk(int w_bf16, int Mp);
+int gemm_k_chunk(int w_bf16);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+hipError_t launch_reduce(const ReduceArgs& r, hipStream_t st);
 
 // Corrected-logit head: per (row, vocabulary tile) the tile's max, sum of
 // exp(y - max) and top-kmax keys of y = z * inv_T (z raw when greedy).
 struct HeadArgs {
-  ASrc a;                     // dense s'
+  PackedA pa;                 // bf16 path: s' hi/lo
+  ASrc a;                     // fp32 path: dense s'
   const void* Ut = nullptr;
   int w_bf16 = 1;
+  int w_packed = 0;
   int V = 0, d = 0;
   int Mp = 0;
   int kmax = 1;               // 1, 4, 8 or 16
@@ -73,6 +95,46 @@ hipError_t launch_merge(const float2* ms_part, const uint64_t* key_part, int row
                         int ntiles, int kt, int k, int kmax, int greedy, int32_t* cand_tok,
                         float* cand_lp, float* lse, hipStream_t st);
 
+// x = E[tok[m]] + h[(m / rpr) * h_req_stride] as packed hi/lo planes [Mp][d]
+// (bf16 heads); rows m >= rows or with tok[m] < 0 are zero.
+struct PrepArgs {
+  const uint16_t* E = nullptr;
+  int d = 0;
+  const int32_t* tok = nullptr;
+  const float* h = nullptr;
+  long h_req_stride = 0;
+  int rpr = 1;
+  int rows = 0, Mp = 0;
+  uint16_t* hi = nullptr;
+  uint16_t* lo = nullptr;
+};
+hipError_t launch_prep_x(const PrepArgs& p, hipStream_t st);
+
+// Columns k .. k + 7 of row m of x for token `tok` (< 0: zero row).
+__device__ __forceinline__ void prep_x_row8(const PrepArgs& p, int m, int k, int tok) {
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = 0.f;
+  if (tok >= 0) {
+    const u32x4 e = *(const u32x4*)(p.E + (long)tok * p.d + k);
+    const float* h = p.h + (long)(m / p.rpr) * p.h_req_stride + k;
+    const float4 h0 = *(const float4*)h, h1 = *(const float4*)(h + 4);
+    y[0] = bf16_to_f32(e[0] & 0xffffu) + h0.x;
+    y[1] = bf16_to_f32(e[0] >> 16) + h0.y;
+    y[2] = bf16_to_f32(e[1] & 0xffffu) + h0.z;
+    y[3] = bf16_to_f32(e[1] >> 16) + h0.w;
+    y[4] = bf16_to_f32(e[2] & 0xffffu) + h1.x;
+    y[5] = bf16_to_f32(e[2] >> 16) + h1.y;
+    y[6] = bf16_to_f32(e[3] & 0xffffu) + h1.z;
+    y[7] = bf16_to_f32(e[3] >> 16) + h1.w;
+  }
+  write_packed8(p.hi, p.lo, p.d, m, k, y);
+}
+
+// Packed block layout of a bf16 matrix W [N][K] (K % 32 == 0): rows padded to
+// a multiple of 16 with zeros; block (nb, kb) at element (nb * K/32 + kb) * 512.
+hipError_t launch_pack_weight(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t st);
+
 // Beam bookkeeping for one depth of R requests.
 struct BeamArgs {
   int R = 0, W = 0, k = 0, D = 0, t = 0, greedy = 0;
@@ -87,13 +149,13 @@ struct BeamArgs {
   float* score_out = nullptr;          // [Mp]
   int32_t* src_out = nullptr;          // [Mp]
   int Mp = 0;
+  PrepArgs prep;                       // next depth's x (bf16 heads; prep.hi null = skip)
 };
 hipError_t launch_beam_init(int R, int W, int Mp, const int32_t* root_tok, int32_t* tok,
-                            float* score, int32_t* src, uint32_t* counters, int n_counters,
-                            hipStream_t st);
+                            float* score, int32_t* src, const PrepArgs* prep, hipStream_t st);
 hipError_t launch_beam_select(const BeamArgs& b, hipStream_t st);
 hipError_t launch_fill_rows(int rows, int Mp, const int32_t* tok_in, int32_t* tok,
-                            int32_t* src, uint32_t* counters, int n_counters, hipStream_t st);
+                            int32_t* src, hipStream_t st);
 
 hipError_t launch_prune(const float* pool_score, const int32_t* pool_parent,
                         const int32_t* n_valid, int R, int D, int W, int B, float beta,

@@ -1,0 +1,48 @@
+// Layout kernels: packing bf16 weights into MFMA-operand blocks, and forming
+// the state-update input x = E[tok] + h_t as packed hi/lo planes.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dt {
+
+// One thread per 16 bytes of the packed output: block (nb, kb), lane l holds
+// row 16 nb + l % 16, K 32 kb + 8 (l / 16) .. + 8; rows >= N are zero.
+__global__ __launch_bounds__(256) void k_pack_weight(const uint16_t* __restrict__ src,
+                                                     uint16_t* __restrict__ dst, int N, int K) {
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int kblocks = K / 32;
+  const long nchunks = (long)((N + 15) / 16) * kblocks * 64;
+  if (gid >= nchunks) return;
+  const int lane = gid & 63;
+  const long blk = gid >> 6;
+  const int nb = blk / kblocks, kb = blk % kblocks;
+  const int n = nb * 16 + (lane & 15), k = kb * 32 + (lane >> 4) * 8;
+  u32x4 v = u32x4{0u, 0u, 0u, 0u};
+  if (n < N) v = *(const u32x4*)(src + (long)n * K + k);
+  *(u32x4*)(dst + gid * 8) = v;
+}
+
+hipError_t launch_pack_weight(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t st) {
+  const long n = (long)((N + 15) / 16) * (K / 32) * 64;
+  hipLaunchKernelGGL(k_pack_weight, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, dst,
+                     N, K);
+  return hipGetLastError();
+}
+
+// One thread per (row m < Mp, 8 consecutive columns).
+__global__ __launch_bounds__(256) void k_prep_x(PrepArgs p) {
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int d8 = p.d / 8;
+  if (gid >= (long)p.Mp * d8) return;
+  const int m = gid / d8, k = (gid % d8) * 8;
+  const int tok = m < p.rows ? p.tok[m] : -1;
+  prep_x_row8(p, m, k, tok);
+}
+
+hipError_t launch_prep_x(const PrepArgs& p, hipStream_t st) {
+  const long n = (long)p.Mp * (p.d / 8);
+  hipLaunchKernelGGL(k_prep_x, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace dt

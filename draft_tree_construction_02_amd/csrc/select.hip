@@ -88,47 +88,52 @@ hipError_t launch_merge(const float2* ms_part, const uint64_t* key_part, int row
 // beam bookkeeping
 // ----------------------------------------------------------------------------
 // Depth-0 frontier: row r*W of request r holds the root (token root_tok[r],
-// score 0, state row r of s0); every other row is empty.  Also zeroes the
-// split-K counters.
+// score 0, state row r of s0); every other row is empty.  With a bf16 head it
+// also forms x for depth 1 (grid covers max(Mp, Mp * d / 8) threads).
 __global__ void k_beam_init(int R, int W, int Mp, const int32_t* __restrict__ root_tok,
-                            int32_t* tok, float* score, int32_t* src, uint32_t* counters,
-                            int n_counters) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+                            int32_t* tok, float* score, int32_t* src, PrepArgs prep) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < Mp) {
     const bool root = i < R * W && i % W == 0;
     tok[i] = root ? root_tok[i / W] : -1;
     score[i] = root ? 0.f : -INFINITY;
-    src[i] = root ? i / W : -1;
+    src[i] = root ? (int)(i / W) : -1;
   }
-  if (i < n_counters) counters[i] = 0u;
+  if (prep.hi) {
+    const int d8 = prep.d / 8;
+    if (i < (long)Mp * d8) {
+      const int m = i / d8, k = (i % d8) * 8;
+      const bool root = m < R * W && m % W == 0;
+      prep_x_row8(prep, m, k, root ? root_tok[m / W] : -1);
+    }
+  }
 }
 
 hipError_t launch_beam_init(int R, int W, int Mp, const int32_t* root_tok, int32_t* tok,
-                            float* score, int32_t* src, uint32_t* counters, int n_counters,
-                            hipStream_t st) {
-  const int n = Mp > n_counters ? Mp : n_counters;
-  hipLaunchKernelGGL(k_beam_init, dim3((n + 255) / 256), dim3(256), 0, st, R, W, Mp, root_tok,
-                     tok, score, src, counters, n_counters);
+                            float* score, int32_t* src, const PrepArgs* prep, hipStream_t st) {
+  PrepArgs p;
+  if (prep) p = *prep;
+  const long n = prep ? (long)Mp * (prep->d / 8) : Mp;
+  hipLaunchKernelGGL(k_beam_init, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, R, W, Mp,
+                     root_tok, tok, score, src, p);
   return hipGetLastError();
 }
 
 // Rows for a stand-alone state update: tokens copied from the caller, state
 // row i of the caller's input for row i, padded rows empty.
 __global__ void k_fill_rows(int rows, int Mp, const int32_t* __restrict__ tok_in, int32_t* tok,
-                            int32_t* src, uint32_t* counters, int n_counters) {
+                            int32_t* src) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < Mp) {
     tok[i] = i < rows ? tok_in[i] : -1;
     src[i] = i < rows ? i : -1;
   }
-  if (i < n_counters) counters[i] = 0u;
 }
 
 hipError_t launch_fill_rows(int rows, int Mp, const int32_t* tok_in, int32_t* tok, int32_t* src,
-                            uint32_t* counters, int n_counters, hipStream_t st) {
-  const int n = Mp > n_counters ? Mp : n_counters;
-  hipLaunchKernelGGL(k_fill_rows, dim3((n + 255) / 256), dim3(256), 0, st, rows, Mp, tok_in, tok,
-                     src, counters, n_counters);
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_fill_rows, dim3((Mp + 255) / 256), dim3(256), 0, st, rows, Mp, tok_in, tok,
+                     src);
   return hipGetLastError();
 }
 
@@ -136,21 +141,24 @@ hipError_t launch_fill_rows(int rows, int Mp, const int32_t* tok_in, int32_t* to
 // scores score_in[i] + cand_lp[i][rank]; the n_t = min(W, n_{t-1} keff) best
 // by (score desc, c asc) take slots 0..n_t-1 in that order.  A candidate's
 // rank is the number of candidates with a larger key (keys are distinct).
+// With a bf16 head the workgroup then forms x = E[tok] + h_{t+1} for its rows.
 constexpr int BEAM_THREADS = 1024;
 
 __global__ __launch_bounds__(BEAM_THREADS) void k_beam_select(BeamArgs b) {
-  extern __shared__ uint64_t keys[];              // [ncand]
+  extern __shared__ uint64_t keys[];              // [ncand], then [W] slot tokens
   const int r = blockIdx.x, tid = threadIdx.x;
   const int base = r * b.W;
   const int n_prev = b.t == 0 ? 1 : b.n_valid[r * b.D + b.t - 1];
   const int keff = b.greedy ? 1 : b.k;
   const int ncand = n_prev * keff;
   const int nkeep = min(b.W, ncand);
+  int32_t* slot_tok = (int32_t*)(keys + b.W * keff);
   for (int c = tid; c < ncand; c += BEAM_THREADS) {
     const int i = c / keff, rk = c % keff;
     const float sc = b.score_in[base + i] + b.cand_lp[(long)(base + i) * b.k + rk];
     keys[c] = make_key(sc, (uint32_t)c);
   }
+  for (int j = tid; j < b.W; j += BEAM_THREADS) slot_tok[j] = -1;
   __syncthreads();
   const long pool = ((long)r * b.D + b.t) * b.W;
   for (int c = tid; c < ncand; c += BEAM_THREADS) {
@@ -167,6 +175,7 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_select(BeamArgs b) {
       b.tok_out[base + rank] = tk;
       b.score_out[base + rank] = sc;
       b.src_out[base + rank] = base + i;
+      slot_tok[rank] = tk;
     }
   }
   for (int j = nkeep + tid; j < b.W; j += BEAM_THREADS) {
@@ -185,12 +194,20 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_select(BeamArgs b) {
       b.score_out[j] = -INFINITY;
       b.src_out[j] = -1;
     }
+  if (b.prep.hi) {
+    __syncthreads();
+    const int d8 = b.prep.d / 8;
+    for (int g = tid; g < b.W * d8; g += BEAM_THREADS) {
+      const int j = g / d8, k = (g % d8) * 8;
+      prep_x_row8(b.prep, base + j, k, slot_tok[j]);
+    }
+  }
 }
 
 hipError_t launch_beam_select(const BeamArgs& b, hipStream_t st) {
   const int ncand_max = b.W * (b.greedy ? 1 : b.k);
-  hipLaunchKernelGGL(k_beam_select, dim3(b.R), dim3(BEAM_THREADS),
-                     (size_t)ncand_max * sizeof(uint64_t), st, b);
+  const size_t lds = (size_t)ncand_max * sizeof(uint64_t) + (size_t)b.W * sizeof(int32_t);
+  hipLaunchKernelGGL(k_beam_select, dim3(b.R), dim3(BEAM_THREADS), lds, st, b);
   return hipGetLastError();
 }
 

@@ -47,6 +47,12 @@ typedef enum {
 
 typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
 
+/* Storage layout of the streamed head weights W1t, W2t and Ut. */
+typedef enum {
+  DT_LAYOUT_ROWMAJOR = 0, /* [N][K] row-major as documented for dt_head          */
+  DT_LAYOUT_PACKED = 1    /* bf16 only: written by pack_head (see there)          */
+} dt_layout;
+
 /* Limits of this build (checked on the host). */
 #define DT_MAX_K 16         /* children per branch                              */
 #define DT_MAX_ROWS 128     /* R * W: branch rows evaluated per head call        */
@@ -69,12 +75,14 @@ typedef enum { DT_F32 = 0, DT_BF16 = 1 } dt_dtype;
  *                     contiguous block)
  * wdtype DT_BF16: all four are bfloat16; DT_F32: all four are float32.
  * d must be a multiple of 128 for DT_BF16 and of 32 for DT_F32.
+ * layout DT_LAYOUT_PACKED (bf16 only) means W1t, W2t and Ut were produced by
+ * pack_head; E is always row-major (rows are gathered by token).
  */
 typedef struct {
   int32_t d;
   int32_t V;
-  int32_t wdtype;      /* dt_dtype */
-  int32_t reserved;
+  int32_t wdtype;      /* dt_dtype  */
+  int32_t layout;      /* dt_layout */
   const void* E;
   const void* W1t;
   const void* W2t;
@@ -86,6 +94,28 @@ const char* dartree_status_string(int status);
 
 /* Library version, (major << 16) | minor. */
 int dartree_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Weight packing (once per model load)                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Device bytes pack_head writes for a row-major bf16 head (0 if invalid). */
+size_t pack_head_bytes(const dt_head* head);
+
+/*
+ * pack_head - copy the streamed bf16 weights W1t [4d][d], W2t [d][4d] and
+ * Ut [V][d] into `dst` (device, pack_head_bytes bytes, caller-owned) in the
+ * packed block layout, and fill `*packed` (host struct) with a head that
+ * points there (E still points to the caller's row-major E).
+ * Packed layout of a matrix [N][K]: rows padded with zeros to a multiple of
+ * 16; 1 KB blocks of 16 rows x 32 columns, block (nb, kb) at element offset
+ * (nb * K/32 + kb) * 512; inside a block, the 8 bf16 at offset 8 l hold row
+ * 16 nb + (l mod 16), columns 32 kb + 8 (l / 16) .. + 7 (l = 0..63).  This is
+ * the operand order of the gfx950 bf16 MFMA, so one wave load instruction
+ * streams one contiguous block.  Asynchronous on `stream`; `dst` must stay
+ * alive while the packed head is used.
+ */
+int pack_head(const dt_head* src, void* dst, size_t dst_bytes, dt_head* packed, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Supertree construction                                                    */
@@ -233,11 +263,12 @@ int tree_attention_verify(const void* q, const void* k_prefix, const void* v_pre
 
 /* Kernel classes that can be timed. */
 typedef enum {
-  DT_K_GEMM1 = 0,   /* state update, first projection (+ GELU)      */
-  DT_K_GEMM2 = 1,   /* state update, second projection (+ residual)  */
-  DT_K_HEAD = 2,    /* corrected-logit head + per-tile softmax/top-k */
-  DT_K_MERGE = 3,   /* per-row merge + beam select                   */
-  DT_K_COUNT = 4
+  DT_K_GEMM1 = 0,   /* state update, first projection (split-K partials)  */
+  DT_K_GEMM2 = 1,   /* state update, second projection (split-K partials) */
+  DT_K_HEAD = 2,    /* corrected-logit head + per-tile softmax/top-k      */
+  DT_K_MERGE = 3,   /* per-row merge and per-request beam select          */
+  DT_K_REDUCE = 4,  /* split-K reductions (GELU / residual epilogues)     */
+  DT_K_COUNT = 5
 } dt_kernel_class;
 
 /*

@@ -12,12 +12,13 @@ from oracle import dartree_oracle as O
 DEV = "cuda:0"
 
 
-def dev_weights(hw: synth.HeadWeights) -> A.Head:
+def dev_weights(hw: synth.HeadWeights, packed: bool = False) -> A.Head:
     def up(a):
         if hw.wdtype == "bf16":
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
-    return A.Head(up(hw.E), up(hw.W1t), up(hw.W2t), up(hw.Ut))
+    head = A.Head(up(hw.E), up(hw.W1t), up(hw.W2t), up(hw.Ut))
+    return head.packed() if packed else head
 
 
 def oracle_head(hw: synth.HeadWeights, cache_u=True) -> O.OracleHead:

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     L = A.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -77,6 +77,28 @@ def test_build_supertree_validation():
     bad.Ut = None
     assert build(bad) == DT_EINVAL
     assert build(fake_head(V=4), k=8) == DT_EINVAL        # k > V
+
+
+def test_pack_head_validation():
+    L = A.lib()
+    out = A.dt_head()
+    f32 = fake_head(d=64, V=100, wdtype=A.DT_F32)
+    assert L.pack_head_bytes(C.byref(f32)) == 0
+    assert L.pack_head(C.byref(f32), 1, 1 << 40, C.byref(out), None) == DT_EINVAL
+    h = fake_head(d=256, V=1000)
+    need = L.pack_head_bytes(C.byref(h))
+    assert need >= 2 * (4 * 256 * 256 * 2) + 1008 * 256 * 2
+    assert L.pack_head(C.byref(h), 1, need - 1, C.byref(out), None) == DT_EWORKSPACE
+    assert L.pack_head(C.byref(h), 1, need, None, None) == DT_EINVAL
+    packed = fake_head(d=256, V=1000)
+    packed.layout = A.DT_LAYOUT_PACKED
+    assert L.pack_head(C.byref(packed), 1, need, C.byref(out), None) == DT_EINVAL
+    bad = fake_head()
+    bad.layout = 5
+    assert build(bad) == DT_EINVAL
+    f32p = fake_head(d=64, V=100, wdtype=A.DT_F32)
+    f32p.layout = A.DT_LAYOUT_PACKED
+    assert build(f32p, k=4) == DT_EINVAL
 
 
 def test_workspace_sizes():

@@ -43,18 +43,26 @@ def small_cases():
 _cache = {}
 
 
-def case_inputs(wl):
-    if wl.name not in _cache:
+def case_inputs(wl, packed=False):
+    key = (wl.name, packed)
+    if key not in _cache:
         hw, req = synth.make_workload_inputs(wl)
-        _cache[wl.name] = (hw, req, dev_weights(hw), oracle_head(hw))
-    return _cache[wl.name]
+        _cache[key] = (hw, req, dev_weights(hw, packed), oracle_head(hw))
+    return _cache[key]
 
 
-@pytest.mark.parametrize("name", list(small_cases()))
-def test_build_prune_mask_match_oracle(name):
+def layouts(names):
+    """(case, packed) pairs: bf16 heads in both weight layouts."""
+    cases = small_cases()
+    return [(n, p) for n in names for p in ((False, True) if cases[n].wdtype == "bf16"
+                                            else (False,))]
+
+
+@pytest.mark.parametrize("name,packed", layouts(small_cases()))
+def test_build_prune_mask_match_oracle(name, packed):
     wl = small_cases()[name]
-    print(f"case {name}", flush=True)
-    hw, req, head, ohead = case_inputs(wl)
+    print(f"case {name} packed={packed}", flush=True)
+    hw, req, head, ohead = case_inputs(wl, packed)
     tol, tau = tolerances(wl.wdtype)
     h, s0, root = dev_requests(req)
     out = A.build_supertree(head, h, s0, root, wl.D, wl.W, wl.k, wl.T)
@@ -88,9 +96,27 @@ def test_build_prune_mask_match_oracle(name):
     print(f"{name}: exemptions {total_exempt}", flush=True)
 
 
+def test_packed_layout_is_the_documented_block_order():
+    # the packed weights, read back, follow the block order the header states
+    wl = small_cases()["bf16_ragged_rows"]          # V = 3001: padded last tile
+    hw, _, head, _ = case_inputs(wl, True)
+    buf = head._packed_buf.cpu().numpy().view(np.uint16)
+    d, V = wl.d, wl.V
+    off = 0
+    for name, N, K in (("W1t", 4 * d, d), ("W2t", d, 4 * d), ("Ut", V, d)):
+        src = getattr(hw, name)
+        Np = (N + 15) // 16 * 16
+        pad = np.zeros((Np, K), np.uint16)
+        pad[:N] = src
+        blocks = pad.reshape(Np // 16, 16, K // 32, 4, 8).transpose(0, 2, 3, 1, 4)
+        got = buf[off:off + Np * K]
+        assert np.array_equal(got, blocks.reshape(-1)), name
+        off += (Np * K * 2 + 255) // 256 * 256 // 2
+
+
 def test_build_is_deterministic():
     wl = small_cases()["bf16_T1"]
-    hw, req, head, _ = case_inputs(wl)
+    hw, req, head, _ = case_inputs(wl, True)
     h, s0, root = dev_requests(req)
     ref = to_np(A.build_supertree(head, h, s0, root, wl.D, wl.W, wl.k, wl.T))
     for _ in range(4):
@@ -99,12 +125,15 @@ def test_build_is_deterministic():
             assert np.array_equal(ref[key].view(np.uint8), got[key].view(np.uint8)), key
 
 
-@pytest.mark.parametrize("name,rows,k,T", [("bf16_T1", 20, 8, 1.0), ("bf16_T1", 16, 4, 0.5),
-                                           ("bf16_T1", 33, 16, 2.0), ("bf16_T0", 7, 8, 0.0),
-                                           ("tiny", 4, 4, 1.0), ("f32_wide", 70, 5, 1.0)])
-def test_corrected_topk_matches_oracle(name, rows, k, T):
+@pytest.mark.parametrize("name,rows,k,T,packed", [
+    ("bf16_T1", 20, 8, 1.0, False), ("bf16_T1", 20, 8, 1.0, True),
+    ("bf16_T1", 16, 4, 0.5, True), ("bf16_T1", 33, 16, 2.0, True),
+    ("bf16_T1", 128, 8, 1.0, True), ("bf16_T1", 64, 1, 1.0, True),
+    ("bf16_T0", 7, 8, 0.0, True), ("bf16_ragged_rows", 50, 3, 0.7, False),
+    ("tiny", 4, 4, 1.0, False), ("f32_wide", 70, 5, 1.0, False)])
+def test_corrected_topk_matches_oracle(name, rows, k, T, packed):
     wl = small_cases()[name]
-    hw, _, head, ohead = case_inputs(wl)
+    hw, _, head, ohead = case_inputs(wl, packed)
     tol, tau = tolerances(wl.wdtype)
     g = np.random.default_rng(rows * 31 + k)
     s = (g.standard_normal((rows, wl.d)) * 2.0).astype(np.float32)
@@ -137,11 +166,13 @@ def test_corrected_topk_matches_oracle(name, rows, k, T):
     print(f"topk {name} exemptions {exempt}")
 
 
-@pytest.mark.parametrize("name,rows", [("bf16_T1", 20), ("bf16_ragged_rows", 18), ("tiny", 4),
-                                       ("f32_wide", 80)])
-def test_state_update_matches_oracle(name, rows):
+@pytest.mark.parametrize("name,rows,packed", [("bf16_T1", 20, False), ("bf16_T1", 20, True),
+                                              ("bf16_ragged_rows", 18, True),
+                                              ("bf16_ragged_rows", 100, False), ("tiny", 4, False),
+                                              ("f32_wide", 80, False)])
+def test_state_update_matches_oracle(name, rows, packed):
     wl = small_cases()[name]
-    hw, _, head, ohead = case_inputs(wl)
+    hw, _, head, ohead = case_inputs(wl, packed)
     g = np.random.default_rng(rows)
     s = g.standard_normal((rows, wl.d)).astype(np.float32)
     tok = g.integers(0, wl.V, rows).astype(np.int32)
