@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-builds", type=int, default=1,
                     help="oracle builds timed for cpu_baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (reference for "
+                         "hardware byte counters) and exit")
     return ap.parse_args()
 
 
@@ -57,6 +60,15 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": src.numel() * 4}))
+        return
 
     from draft_tree_construction_02_amd import _abi as A
     from draft_tree_construction_02_amd import synth

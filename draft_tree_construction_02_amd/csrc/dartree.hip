@@ -192,11 +192,28 @@ struct DepthIo {
   int rows_out;
 };
 
-// s' = s_parent + GELU(x W1) W2: two split-K GEMMs, each followed by its
-// in-order reduction.  bf16 heads read x from the packed planes in w.x_*.
+// s' = s_parent + GELU(x W1) W2 with x = E[tok] + h_t: (bf16 heads) x is
+// formed as packed hi/lo planes, then two split-K GEMMs, each followed by its
+// in-order reduction.
 hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hipStream_t st) {
   const int bf = hd->wdtype == DT_BF16, d = hd->d;
   const int packed = hd->layout == DT_LAYOUT_PACKED;
+  hipError_t e = hipSuccess;
+  if (bf) {
+    PrepArgs pr;
+    pr.E = (const uint16_t*)hd->E;
+    pr.d = d;
+    pr.tok = io.tok;
+    pr.h = io.h;
+    pr.h_req_stride = io.h_req_stride;
+    pr.rpr = io.rpr;
+    pr.rows = io.rows;
+    pr.Mp = w.Mp;
+    pr.hi = w.x_hi;
+    pr.lo = w.x_lo;
+    e = timed(DT_K_REDUCE, st, [&] { return launch_prep_x(pr, st); });
+    if (e != hipSuccess) return e;
+  }
   GemmArgs g1;
   g1.pa = PackedA{w.x_hi, w.x_lo, d};
   g1.a.gather = 1;
@@ -215,7 +232,7 @@ hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hip
   g1.Mp = w.Mp;
   g1.splits = w.splits1;
   g1.part = w.part;
-  hipError_t e = timed(DT_K_GEMM1, st, [&] { return launch_gemm(g1, st); });
+  e = timed(DT_K_GEMM1, st, [&] { return launch_gemm(g1, st); });
   if (e != hipSuccess) return e;
   ReduceArgs r1;
   r1.part = w.part;
@@ -342,20 +359,8 @@ int build_supertree(const dt_head* head, const float* h, const float* s0, const 
   StepWs w = carve_step(c, head, R * W, k);
   const int d = head->d, rows = R * W;
   const bool greedy = T == 0.f;
-  const bool bf = head->wdtype == DT_BF16;
 
-  PrepArgs prep;
-  prep.E = (const uint16_t*)head->E;
-  prep.d = d;
-  prep.h = h;
-  prep.h_req_stride = (long)D * d;
-  prep.rpr = W;
-  prep.rows = rows;
-  prep.Mp = w.Mp;
-  prep.hi = w.x_hi;
-  prep.lo = w.x_lo;
-  hipError_t e = launch_beam_init(R, W, w.Mp, root_tok, w.tok[0], w.score[0], w.src[0],
-                                  bf ? &prep : nullptr, st);
+  hipError_t e = launch_beam_init(R, W, w.Mp, root_tok, w.tok[0], w.score[0], w.src[0], st);
   for (int t = 0; t < D && e == hipSuccess; ++t) {
     const int cur = t & 1, nxt = cur ^ 1;
     DepthIo io;
@@ -385,10 +390,6 @@ int build_supertree(const dt_head* head, const float* h, const float* s0, const 
     b.score_out = w.score[nxt];
     b.src_out = w.src[nxt];
     b.Mp = w.Mp;
-    if (bf && t + 1 < D) {
-      b.prep = prep;
-      b.prep.h = h + (long)(t + 1) * d;
-    }
     e = timed(DT_K_MERGE, st, [&] { return launch_beam_select(b, st); });
   }
   return e == hipSuccess ? DT_OK : DT_EHIP;
@@ -415,20 +416,6 @@ int state_update(const dt_head* head, const float* s_in, const int32_t* tok, con
   Carver c(workspace);
   StepWs w = carve_step(c, head, rows, 1);
   hipError_t e = launch_fill_rows(rows, w.Mp, tok, w.tok[0], w.src[0], st);
-  if (e == hipSuccess && head->wdtype == DT_BF16) {
-    PrepArgs prep;
-    prep.E = (const uint16_t*)head->E;
-    prep.d = head->d;
-    prep.tok = w.tok[0];
-    prep.h = h;
-    prep.h_req_stride = 0;
-    prep.rpr = 1;
-    prep.rows = rows;
-    prep.Mp = w.Mp;
-    prep.hi = w.x_hi;
-    prep.lo = w.x_lo;
-    e = launch_prep_x(prep, st);
-  }
   if (e == hipSuccess) {
     DepthIo io;
     io.s_prev = s_in;

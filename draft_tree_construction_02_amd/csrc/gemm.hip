@@ -29,18 +29,48 @@
 
 namespace dt {
 
-constexpr int NT = 256;               // threads per workgroup
-constexpr int NWAVES = NT / WAVE;     // 4
-constexpr int NW = 2;                 // 16-column MFMA tiles per wave
-constexpr int TN_B = NWAVES * NW * 16;   // 128 columns per bf16 workgroup
+// Tile shape of the bf16 path: NW_* 16-column MFMA tiles per wave (so
+// 64 NW_* columns per workgroup) and register prefetch PF_* (1: the next
+// K iteration's weights are loaded before the current MFMAs; 0: occupancy
+// alone hides the load latency).
+#ifndef DT_NW_HEAD
+#define DT_NW_HEAD 2
+#endif
+#ifndef DT_PF_HEAD
+#define DT_PF_HEAD 0
+#endif
+#ifndef DT_NW_GEMM
+#define DT_NW_GEMM 2
+#endif
+#ifndef DT_PF_GEMM
+#define DT_PF_GEMM 0
+#endif
+#ifndef DT_WV_HEAD
+#define DT_WV_HEAD 4
+#endif
+#ifndef DT_WV_GEMM
+#define DT_WV_GEMM 4
+#endif
+#ifndef DT_KC_B
+#define DT_KC_B 128
+#endif
+// 1: each wave reads its activation blocks straight from L2 (no LDS staging,
+// no barrier in the K loop); 0: the workgroup stages them once in LDS.
+#ifndef DT_DIRECT_A
+#define DT_DIRECT_A 0
+#endif
+
+constexpr int NT = 256;               // threads per workgroup (fp32 path, helpers)
+constexpr int TN_HEAD = DT_WV_HEAD * DT_NW_HEAD * 16;
+constexpr int TN_GEMM = DT_WV_GEMM * DT_NW_GEMM * 16;
 constexpr int TN_F = 64;              // columns per fp32 workgroup
-constexpr int KC_B = 128;             // K staged per LDS chunk (bf16 path)
+constexpr int KC_B = DT_KC_B;         // K staged per LDS chunk (bf16 path)
 constexpr int KC_F = 32;              // K staged per LDS chunk (fp32 path)
 constexpr int CPAD = 4;               // C tile row padding (floats)
 constexpr int BLK = 512;              // bf16 elements per packed block (1 KB)
 
-int gemm_tile_n(int w_bf16) { return w_bf16 ? TN_B : TN_F; }
-int head_tile_n(int w_bf16) { return w_bf16 ? TN_B : TN_F; }
+int gemm_tile_n(int w_bf16) { return w_bf16 ? TN_GEMM : TN_F; }
+int head_tile_n(int w_bf16) { return w_bf16 ? TN_HEAD : TN_F; }
 int gemm_k_chunk(int w_bf16) { return w_bf16 ? KC_B : KC_F; }
 
 __device__ __forceinline__ float gelu_f(float y) {
@@ -52,12 +82,11 @@ __device__ __forceinline__ float gelu_f(float y) {
 // ----------------------------------------------------------------------------
 // LDS chunk layout: [hl][mt][kb][512] with kb the 32-wide K block inside the
 // chunk; every block is copied whole (64 lanes x 16 B).
-template <int MT, int KC>
+template <int MT, int KC, int WV>
 struct AStagePacked {
   static constexpr int KB = KC / 32;                  // blocks per row tile
   static constexpr int NBLK = 2 * MT * KB;            // blocks per chunk
-  static constexpr int PER_WAVE = NBLK / NWAVES;      // blocks per wave
-  static_assert(NBLK % NWAVES == 0, "chunk must split over waves");
+  static constexpr int PER_WAVE = (NBLK + WV - 1) / WV;   // blocks per wave
   u32x4 v[PER_WAVE];
 
   __device__ __forceinline__ void issue(const PackedA& a, int k) {
@@ -65,18 +94,20 @@ struct AStagePacked {
     const int kblocks = a.K / 32;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-      const int bi = wave + i * NWAVES;
-      const int hl = bi / (MT * KB), rem = bi % (MT * KB), mt = rem / KB, kb = rem % KB;
-      const uint16_t* src = (hl ? a.lo : a.hi) + ((long)mt * kblocks + k / 32 + kb) * BLK;
-      v[i] = *(const u32x4*)(src + lane * 8);
+      const int bi = wave + i * WV;
+      if (NBLK % WV == 0 || bi < NBLK) {
+        const int hl = bi / (MT * KB), rem = bi % (MT * KB), mt = rem / KB, kb = rem % KB;
+        const uint16_t* src = (hl ? a.lo : a.hi) + ((long)mt * kblocks + k / 32 + kb) * BLK;
+        v[i] = *(const u32x4*)(src + lane * 8);
+      }
     }
   }
   __device__ __forceinline__ void commit(uint16_t* As) const {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-      const int bi = wave + i * NWAVES;
-      *(u32x4*)(As + bi * BLK + lane * 8) = v[i];
+      const int bi = wave + i * WV;
+      if (NBLK % WV == 0 || bi < NBLK) *(u32x4*)(As + bi * BLK + lane * 8) = v[i];
     }
   }
 };
@@ -84,7 +115,7 @@ struct AStagePacked {
 // Weight fragments of one 128-K iteration: b[c][j] is the 16 x 32 block of
 // column tile c and K step j, in MFMA operand order (lane l: row l % 16,
 // K 8 (l / 16) .. + 8 of the step).
-template <bool PACKED>
+template <int NW, bool PACKED>
 __device__ __forceinline__ void load_b(u32x4 (&b)[NW][4], const uint16_t* __restrict__ Wt,
                                        int K, int col0, int N, int kb, int lane) {
 #pragma unroll
@@ -114,7 +145,7 @@ __device__ __forceinline__ void load_b(u32x4 (&b)[NW][4], const uint16_t* __rest
   }
 }
 
-template <int MT, int KC>
+template <int MT, int KC, int NW>
 __device__ __forceinline__ void mma_iter(const uint16_t* As, int it, const u32x4 (&b)[NW][4],
                                          f32x4 (&acc)[NW][MT], int lane) {
   constexpr int KB = KC / 32;
@@ -138,24 +169,26 @@ __device__ __forceinline__ void mma_iter(const uint16_t* As, int it, const u32x4
   }
 }
 
-template <int MT, int NBUF>
+template <int MT, int NBUF, int NW, int WV>
 struct BfCfg {
   static constexpr int Mp = 16 * MT;
   static constexpr int KC = KC_B;
+  static constexpr int TN = WV * NW * 16;
   static constexpr int ABUF = 2 * MT * (KC / 32) * BLK;     // bf16 per buffer
   static constexpr int A_BYTES = NBUF * ABUF * 2;
-  static constexpr int C_BYTES = Mp * (TN_B + CPAD) * 4;
+  static constexpr int C_BYTES = Mp * (TN + CPAD) * 4;
   static constexpr int LDS = A_BYTES > C_BYTES ? A_BYTES : C_BYTES;
 };
 
-// Accumulates Y[0..Mp)[n0..n0+128) over K range [k0, k0 + klen).  On return
-// acc[c][mt] holds rows 16 mt + lane % 16, columns n0 + 32 wave + 16 c +
+// Accumulates Y[0..Mp)[n0..n0+TN) over K range [k0, k0 + klen).  On return
+// acc[c][mt] holds rows 16 mt + lane % 16, columns n0 + 16 NW wave + 16 c +
 // 4 (lane / 16) + i (i = 0..3) in element i.
-template <int MT, int NBUF, bool PW>
-__device__ __forceinline__ void tile_bf16(const PackedA& a, const uint16_t* __restrict__ Wt,
+template <int MT, int NBUF, bool PW, int NW, int PF, int WV, class Stage, class ASource>
+__device__ __forceinline__ void tile_bf16(const ASource& a, const uint16_t* __restrict__ Wt,
                                           int N, int n0, int k0, int klen, unsigned char* smem,
                                           f32x4 (&acc)[NW][MT]) {
-  using C = BfCfg<MT, NBUF>;
+  using C = BfCfg<MT, NBUF, NW, WV>;
+  constexpr int IPS = C::KC / 128;          // 128-K iterations per staged chunk
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   uint16_t* As = (uint16_t*)smem;
 #pragma unroll
@@ -163,28 +196,79 @@ __device__ __forceinline__ void tile_bf16(const PackedA& a, const uint16_t* __re
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  AStagePacked<MT, C::KC> st;
+  Stage st;
   const int col0 = n0 + wave * NW * 16;
-  u32x4 bc[NW][4], bn[NW][4];
-  load_b<PW>(bc, Wt, a.K, col0, N, k0, lane);
-  st.issue(a, k0);
-  st.commit(As);
-  __syncthreads();
-
   const int nst = klen / C::KC;
-  for (int s = 0; s < nst; ++s) {
-    const uint16_t* Ab = As + (NBUF == 2 ? (s & 1) * C::ABUF : 0);
-    const bool more = s + 1 < nst;
-    if (more) load_b<PW>(bn, Wt, a.K, col0, N, k0 + (s + 1) * C::KC, lane);
-    if (more) st.issue(a, k0 + (s + 1) * C::KC);
-    mma_iter<MT, C::KC>(Ab, 0, bc, acc, lane);
-    if (more) {
-      if (NBUF == 1) __syncthreads();
-      st.commit(As + (NBUF == 2 ? ((s + 1) & 1) * C::ABUF : 0));
+  if constexpr (PF != 0) {
+    u32x4 bc[NW][4], bn[NW][4];
+    load_b<NW, PW>(bc, Wt, a.K, col0, N, k0, lane);
+    st.issue(a, k0);
+    st.commit(As);
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+      const uint16_t* Ab = As + (NBUF == 2 ? (s & 1) * C::ABUF : 0);
+      const bool more = s + 1 < nst;
+      static_assert(IPS == 1, "register prefetch path stages one iteration per chunk");
+      if (more) load_b<NW, PW>(bn, Wt, a.K, col0, N, k0 + (s + 1) * C::KC, lane);
+      if (more) st.issue(a, k0 + (s + 1) * C::KC);
+      mma_iter<MT, C::KC, NW>(Ab, 0, bc, acc, lane);
+      if (more) {
+        if (NBUF == 1) __syncthreads();
+        st.commit(As + (NBUF == 2 ? ((s + 1) & 1) * C::ABUF : 0));
 #pragma unroll
-      for (int c = 0; c < NW; ++c)
+        for (int c = 0; c < NW; ++c)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bc[c][q] = bn[c][q];
+          for (int q = 0; q < 4; ++q) bc[c][q] = bn[c][q];
+      }
+      __syncthreads();
+    }
+  } else if constexpr (DT_DIRECT_A != 0) {
+    // activation fragments straight from the packed planes in L2
+    const int kblocks = a.K / 32;
+    for (int s = 0; s < klen / 128; ++s) {
+      const int k = k0 + s * 128;
+      u32x4 b[NW][4], ah[MT][4], al[MT][4];
+      load_b<NW, PW>(b, Wt, a.K, col0, N, k, lane);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const long off = ((long)mt * kblocks + k / 32 + j) * BLK + lane * 8;
+          ah[mt][j] = *(const u32x4*)(a.hi + off);
+          al[mt][j] = *(const u32x4*)(a.lo + off);
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+          for (int c = 0; c < NW; ++c)
+            acc[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, b[c][j]), __builtin_bit_cast(bf16x8, ah[mt][j]),
+                acc[c][mt], 0, 0, 0);
+#pragma unroll
+          for (int c = 0; c < NW; ++c)
+            acc[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, b[c][j]), __builtin_bit_cast(bf16x8, al[mt][j]),
+                acc[c][mt], 0, 0, 0);
+        }
+    }
+    __syncthreads();
+  } else {
+    // no register prefetch: weights and the activation chunk of iteration s
+    // are requested together; other resident waves cover the latency
+    for (int s = 0; s < nst; ++s) {
+      const int k = k0 + s * C::KC;
+      uint16_t* Ab = As + (NBUF == 2 ? (s & 1) * C::ABUF : 0);
+      u32x4 b[IPS][NW][4];
+#pragma unroll
+      for (int it = 0; it < IPS; ++it) load_b<NW, PW>(b[it], Wt, a.K, col0, N, k + 128 * it, lane);
+      st.issue(a, k);
+      if (NBUF == 1 && s > 0) __syncthreads();
+      st.commit(Ab);
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < IPS; ++it) mma_iter<MT, C::KC, NW>(Ab, it, b[it], acc, lane);
     }
     __syncthreads();
   }
@@ -289,14 +373,17 @@ __device__ __forceinline__ float* tile_f32(const ASrc& src, const float* __restr
 // split-K partial products
 // ----------------------------------------------------------------------------
 template <int MT, int NBUF, bool PW>
-__global__ __launch_bounds__(NT) void k_gemm_bf16(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[BfCfg<MT, NBUF>::LDS];
+__global__ __launch_bounds__(64 * DT_WV_GEMM) void k_gemm_bf16(GemmArgs g) {
+  constexpr int NW = DT_NW_GEMM, WV = DT_WV_GEMM;
+  using Cfg = BfCfg<MT, NBUF, NW, WV>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg::LDS];
   constexpr int Mp = 16 * MT;
   const int tile = blockIdx.x, split = blockIdx.y;
-  const int klen = g.pa.K / g.splits, k0 = split * klen;
-  const int n0 = tile * TN_B;
+  const int klen = g.K / g.splits, k0 = split * klen;
+  const int n0 = tile * TN_GEMM;
   f32x4 acc[NW][MT];
-  tile_bf16<MT, NBUF, PW>(g.pa, (const uint16_t*)g.Wt, g.N, n0, k0, klen, smem, acc);
+  tile_bf16<MT, NBUF, PW, NW, DT_PF_GEMM, WV, AStagePacked<MT, Cfg::KC, WV>>(
+      g.pa, (const uint16_t*)g.Wt, g.N, n0, k0, klen, smem, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
 #pragma unroll
@@ -341,6 +428,7 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs r) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = 0.f;
   if (m < r.rows) {
+#pragma unroll 8
     for (int s = 0; s < r.splits; ++s) {
       const float* p = r.part + ((long)s * r.Mp + m) * r.N + n;
       const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
@@ -376,10 +464,11 @@ hipError_t launch_reduce(const ReduceArgs& r, hipStream_t st) {
 // ----------------------------------------------------------------------------
 // corrected-logit head with fused per-tile log-softmax statistics and top-k
 // ----------------------------------------------------------------------------
-template <int MT, int KMAX, int TN>
+template <int MT, int KMAX, int TN, int THREADS>
 __device__ __forceinline__ void head_epilogue(const HeadArgs& p, const float* Cs, int tile) {
   constexpr int Mp = 16 * MT;
-  constexpr int G = NT / Mp;              // threads per row
+  constexpr int G = THREADS / Mp;         // threads per row (power of two <= 64)
+  static_assert(G >= 1 && G <= 64, "row group must fit in a wave");
   const int tid = threadIdx.x, m = tid / G, q = tid % G;
   const int n0 = tile * TN, ntiles = gridDim.x;
   const int nvalid = min(TN, p.V - n0);
@@ -412,11 +501,15 @@ __device__ __forceinline__ void head_epilogue(const HeadArgs& p, const float* Cs
 }
 
 template <int MT, int NBUF, int KMAX, bool PW>
-__global__ __launch_bounds__(NT) void k_head_bf16(HeadArgs p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[BfCfg<MT, NBUF>::LDS];
-  const int tile = blockIdx.x, n0 = tile * TN_B;
+__global__ __launch_bounds__(64 * DT_WV_HEAD) void k_head_bf16(HeadArgs p) {
+  constexpr int NW = DT_NW_HEAD;
+  constexpr int TN = TN_HEAD;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[BfCfg<MT, NBUF, NW, DT_WV_HEAD>::LDS];
+  const int tile = blockIdx.x, n0 = tile * TN;
   f32x4 acc[NW][MT];
-  tile_bf16<MT, NBUF, PW>(p.pa, (const uint16_t*)p.Ut, p.V, n0, 0, p.d, smem, acc);
+  tile_bf16<MT, NBUF, PW, NW, DT_PF_HEAD, DT_WV_HEAD,
+            AStagePacked<MT, BfCfg<MT, NBUF, NW, DT_WV_HEAD>::KC, DT_WV_HEAD>>(
+      p.pa, (const uint16_t*)p.Ut, p.V, n0, 0, p.d, smem, acc);
   // accumulators -> LDS C tile (the A buffers are free after the last barrier)
   float* Cs = (float*)smem;
   const float scale = p.greedy ? 1.f : p.inv_T;
@@ -427,11 +520,11 @@ __global__ __launch_bounds__(NT) void k_head_bf16(HeadArgs p) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const f32x4 v = acc[c][mt];
-      *(float4*)(Cs + (16 * mt + r) * (TN_B + CPAD) + wave * NW * 16 + c * 16 + 4 * q) =
+      *(float4*)(Cs + (16 * mt + r) * (TN + CPAD) + wave * NW * 16 + c * 16 + 4 * q) =
           make_float4(v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale);
     }
   __syncthreads();
-  head_epilogue<MT, KMAX, TN_B>(p, Cs, tile);
+  head_epilogue<MT, KMAX, TN, 64 * DT_WV_HEAD>(p, Cs, tile);
 }
 
 template <int MT, int KMAX>
@@ -440,7 +533,7 @@ __global__ __launch_bounds__(NT) void k_head_f32(HeadArgs p) {
   const int tile = blockIdx.x;
   const float* Cs = tile_f32<MT, false>(p.a, (const float*)p.Ut, p.d, p.V, tile * TN_F, 0, p.d,
                                         p.greedy ? 1.f : p.inv_T, smem);
-  head_epilogue<MT, KMAX, TN_F>(p, Cs, tile);
+  head_epilogue<MT, KMAX, TN_F, NT>(p, Cs, tile);
 }
 
 // ----------------------------------------------------------------------------
@@ -448,14 +541,15 @@ __global__ __launch_bounds__(NT) void k_head_f32(HeadArgs p) {
 // ----------------------------------------------------------------------------
 template <int MT>
 static hipError_t gemm_mt(const GemmArgs& g, hipStream_t st) {
-  const int TN = g.w_bf16 ? TN_B : TN_F;
+  const int TN = g.w_bf16 ? TN_GEMM : TN_F;
   dim3 grid((g.N + TN - 1) / TN, g.splits);
   if (g.w_bf16) {
     constexpr int NB = MT >= 8 ? 1 : 2;
+    const dim3 blk(64 * DT_WV_GEMM);
     if (g.w_packed)
-      hipLaunchKernelGGL((k_gemm_bf16<MT, NB, true>), grid, dim3(NT), 0, st, g);
+      hipLaunchKernelGGL((k_gemm_bf16<MT, NB, true>), grid, blk, 0, st, g);
     else
-      hipLaunchKernelGGL((k_gemm_bf16<MT, NB, false>), grid, dim3(NT), 0, st, g);
+      hipLaunchKernelGGL((k_gemm_bf16<MT, NB, false>), grid, blk, 0, st, g);
   } else {
     if (g.a.gather)
       hipLaunchKernelGGL((k_gemm_f32<MT, true>), grid, dim3(NT), 0, st, g);
@@ -477,14 +571,14 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
 
 template <int MT, int KMAX>
 static hipError_t head_mk(const HeadArgs& p, hipStream_t st) {
-  const int TN = p.w_bf16 ? TN_B : TN_F;
+  const int TN = p.w_bf16 ? TN_HEAD : TN_F;
   dim3 grid((p.V + TN - 1) / TN);
   if (p.w_bf16) {
     constexpr int NB = MT >= 8 ? 1 : 2;
     if (p.w_packed)
-      hipLaunchKernelGGL((k_head_bf16<MT, NB, KMAX, true>), grid, dim3(NT), 0, st, p);
+      hipLaunchKernelGGL((k_head_bf16<MT, NB, KMAX, true>), grid, dim3(64 * DT_WV_HEAD), 0, st, p);
     else
-      hipLaunchKernelGGL((k_head_bf16<MT, NB, KMAX, false>), grid, dim3(NT), 0, st, p);
+      hipLaunchKernelGGL((k_head_bf16<MT, NB, KMAX, false>), grid, dim3(64 * DT_WV_HEAD), 0, st, p);
   } else {
     hipLaunchKernelGGL((k_head_f32<MT, KMAX>), grid, dim3(NT), 0, st, p);
   }

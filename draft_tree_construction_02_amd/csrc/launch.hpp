@@ -37,7 +37,7 @@ enum Epi { EPI_GELU = 0, EPI_RESID = 1 };
 
 // Split-K partial products part[split][Mp][N] of Y = A Wt^T, Wt [N][K].
 struct GemmArgs {
-  PackedA pa;                 // bf16 path
+  PackedA pa;                 // bf16 path, packed activation planes
   ASrc a;                     // fp32 path
   const void* Wt = nullptr;
   int w_bf16 = 1;
@@ -95,8 +95,8 @@ hipError_t launch_merge(const float2* ms_part, const uint64_t* key_part, int row
                         int ntiles, int kt, int k, int kmax, int greedy, int32_t* cand_tok,
                         float* cand_lp, float* lse, hipStream_t st);
 
-// x = E[tok[m]] + h[(m / rpr) * h_req_stride] as packed hi/lo planes [Mp][d]
-// (bf16 heads); rows m >= rows or with tok[m] < 0 are zero.
+// x = E[tok[m]] + h[(m / rpr) * h_req_stride] written as packed hi/lo planes
+// [Mp][d] (bf16 heads); rows m >= rows or with tok[m] < 0 are zero.
 struct PrepArgs {
   const uint16_t* E = nullptr;
   int d = 0;
@@ -109,27 +109,6 @@ struct PrepArgs {
   uint16_t* lo = nullptr;
 };
 hipError_t launch_prep_x(const PrepArgs& p, hipStream_t st);
-
-// Columns k .. k + 7 of row m of x for token `tok` (< 0: zero row).
-__device__ __forceinline__ void prep_x_row8(const PrepArgs& p, int m, int k, int tok) {
-  float y[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) y[i] = 0.f;
-  if (tok >= 0) {
-    const u32x4 e = *(const u32x4*)(p.E + (long)tok * p.d + k);
-    const float* h = p.h + (long)(m / p.rpr) * p.h_req_stride + k;
-    const float4 h0 = *(const float4*)h, h1 = *(const float4*)(h + 4);
-    y[0] = bf16_to_f32(e[0] & 0xffffu) + h0.x;
-    y[1] = bf16_to_f32(e[0] >> 16) + h0.y;
-    y[2] = bf16_to_f32(e[1] & 0xffffu) + h0.z;
-    y[3] = bf16_to_f32(e[1] >> 16) + h0.w;
-    y[4] = bf16_to_f32(e[2] & 0xffffu) + h1.x;
-    y[5] = bf16_to_f32(e[2] >> 16) + h1.y;
-    y[6] = bf16_to_f32(e[3] & 0xffffu) + h1.z;
-    y[7] = bf16_to_f32(e[3] >> 16) + h1.w;
-  }
-  write_packed8(p.hi, p.lo, p.d, m, k, y);
-}
 
 // Packed block layout of a bf16 matrix W [N][K] (K % 32 == 0): rows padded to
 // a multiple of 16 with zeros; block (nb, kb) at element (nb * K/32 + kb) * 512.
@@ -149,10 +128,9 @@ struct BeamArgs {
   float* score_out = nullptr;          // [Mp]
   int32_t* src_out = nullptr;          // [Mp]
   int Mp = 0;
-  PrepArgs prep;                       // next depth's x (bf16 heads; prep.hi null = skip)
 };
 hipError_t launch_beam_init(int R, int W, int Mp, const int32_t* root_tok, int32_t* tok,
-                            float* score, int32_t* src, const PrepArgs* prep, hipStream_t st);
+                            float* score, int32_t* src, hipStream_t st);
 hipError_t launch_beam_select(const BeamArgs& b, hipStream_t st);
 hipError_t launch_fill_rows(int rows, int Mp, const int32_t* tok_in, int32_t* tok,
                             int32_t* src, hipStream_t st);

@@ -1,5 +1,6 @@
-// Layout kernels: packing bf16 weights into MFMA-operand blocks, and forming
-// the state-update input x = E[tok] + h_t as packed hi/lo planes.
+// Layout kernels: packing of bf16 weights into MFMA-operand blocks (once per
+// model load) and forming the state-update input x = E[tok] + h_t as packed
+// hi/lo planes (once per depth).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -29,14 +30,30 @@ hipError_t launch_pack_weight(const uint16_t* src, uint16_t* dst, int N, int K, 
   return hipGetLastError();
 }
 
-// One thread per (row m < Mp, 8 consecutive columns).
+// One thread per (row m < Mp, 8 consecutive columns k).
 __global__ __launch_bounds__(256) void k_prep_x(PrepArgs p) {
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const int d8 = p.d / 8;
   if (gid >= (long)p.Mp * d8) return;
   const int m = gid / d8, k = (gid % d8) * 8;
   const int tok = m < p.rows ? p.tok[m] : -1;
-  prep_x_row8(p, m, k, tok);
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = 0.f;
+  if (tok >= 0) {
+    const u32x4 e = *(const u32x4*)(p.E + (long)tok * p.d + k);
+    const float* h = p.h + (long)(m / p.rpr) * p.h_req_stride + k;
+    const float4 h0 = *(const float4*)h, h1 = *(const float4*)(h + 4);
+    y[0] = bf16_to_f32(e[0] & 0xffffu) + h0.x;
+    y[1] = bf16_to_f32(e[0] >> 16) + h0.y;
+    y[2] = bf16_to_f32(e[1] & 0xffffu) + h0.z;
+    y[3] = bf16_to_f32(e[1] >> 16) + h0.w;
+    y[4] = bf16_to_f32(e[2] & 0xffffu) + h1.x;
+    y[5] = bf16_to_f32(e[2] >> 16) + h1.y;
+    y[6] = bf16_to_f32(e[3] & 0xffffu) + h1.z;
+    y[7] = bf16_to_f32(e[3] >> 16) + h1.w;
+  }
+  write_packed8(p.hi, p.lo, p.d, m, k, y);
 }
 
 hipError_t launch_prep_x(const PrepArgs& p, hipStream_t st) {

@@ -3,30 +3,51 @@
 //
 // Every selection orders by a total key (value desc, index asc) packed into a
 // u64, so ties are broken identically on every run; no floating-point atomics.
+#include "../../include/dartree.h"
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace dt {
 
 // ----------------------------------------------------------------------------
-// merge: one workgroup per row
+// merge: one workgroup (8 waves) per row
 // ----------------------------------------------------------------------------
+// Each thread folds up to MERGE_BATCH tiles per pass (loads issued together),
+// each wave reduces by a butterfly, then lanes 0..7 of wave 0 reduce the 8
+// wave results by another butterfly.  The (max, sum) pairs combine in the same
+// fixed tree, so the result does not depend on timing.
+constexpr int MERGE_THREADS = 512;
+
 template <int KMAX>
-__global__ __launch_bounds__(256) void k_merge(const float2* __restrict__ ms_part,
-                                               const uint64_t* __restrict__ key_part,
-                                               int ntiles, int kt, int k, int greedy,
-                                               int32_t* __restrict__ cand_tok,
-                                               float* __restrict__ cand_lp,
-                                               float* __restrict__ lse) {
+__global__ __launch_bounds__(MERGE_THREADS) void k_merge(const float2* __restrict__ ms_part,
+                                                         const uint64_t* __restrict__ key_part,
+                                                         int ntiles, int kt, int k, int greedy,
+                                                         int32_t* __restrict__ cand_tok,
+                                                         float* __restrict__ cand_lp,
+                                                         float* __restrict__ lse) {
+  constexpr int MERGE_BATCH = KMAX >= 16 ? 2 : 4;
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   MaxSum ms{-INFINITY, 0.f};
   TopK<KMAX> tk;
   tk.clear();
-  for (int t = tid; t < ntiles; t += 256) {
-    const long o = (long)row * ntiles + t;
-    const float2 p = ms_part[o];
-    ms.combine(p.x, p.y);
-    for (int i = 0; i < kt; ++i) tk.insert(key_part[o * kt + i]);
+  const float2* mrow = ms_part + (long)row * ntiles;
+  const uint64_t* krow = key_part + (long)row * ntiles * kt;
+  for (int t0 = 0; t0 < ntiles; t0 += MERGE_THREADS * MERGE_BATCH) {
+    float2 p[MERGE_BATCH];
+    uint64_t kv[MERGE_BATCH][KMAX];
+#pragma unroll
+    for (int b = 0; b < MERGE_BATCH; ++b) {
+      const int t = t0 + b * MERGE_THREADS + tid;
+      p[b] = t < ntiles ? mrow[t] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) kv[b][i] = (t < ntiles && i < kt) ? krow[(long)t * kt + i] : 0ull;
+    }
+#pragma unroll
+    for (int b = 0; b < MERGE_BATCH; ++b) {
+      ms.combine(p[b].x, p[b].y);
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) tk.insert(kv[b][i]);
+    }
   }
   for (int off = 1; off < 64; off <<= 1) {
     const float m2 = __shfl_xor(ms.m, off, 64);
@@ -34,36 +55,38 @@ __global__ __launch_bounds__(256) void k_merge(const float2* __restrict__ ms_par
     ms.combine(m2, s2);
   }
   tk.reduce_lanes(64);
-  __shared__ float2 wms[4];
-  __shared__ uint64_t wkeys[4][KMAX];
+  constexpr int NWV = MERGE_THREADS / 64;
+  __shared__ float2 wms[NWV];
+  __shared__ uint64_t wkeys[NWV][KMAX];
   if (lane == 0) {
     wms[wave] = make_float2(ms.m, ms.s);
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) wkeys[wave][i] = tk.v[i];
   }
   __syncthreads();
-  if (tid != 0) return;
-  MaxSum tot{wms[0].x, wms[0].y};
+  if (wave != 0) return;
+  const int src = lane < NWV ? lane : 0;
+  MaxSum tot{lane < NWV ? wms[src].x : -INFINITY, lane < NWV ? wms[src].y : 0.f};
   TopK<KMAX> all;
 #pragma unroll
-  for (int i = 0; i < KMAX; ++i) all.v[i] = wkeys[0][i];
-  for (int w = 1; w < 4; ++w) {
-    tot.combine(wms[w].x, wms[w].y);
-    uint64_t o[KMAX];
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) o[i] = wkeys[w][i];
-    all.merge(o);
+  for (int i = 0; i < KMAX; ++i) all.v[i] = lane < NWV ? wkeys[src][i] : 0ull;
+  for (int off = 1; off < NWV; off <<= 1) {
+    const float m2 = __shfl_xor(tot.m, off, 64);
+    const float s2 = __shfl_xor(tot.s, off, 64);
+    tot.combine(m2, s2);
   }
+  all.reduce_lanes(NWV);
+  if (lane != 0) return;
   const float L = greedy ? tot.m : tot.m + logf(tot.s);
   lse[row] = L;
-  for (int i = 0; i < k; ++i) {
+  for (int j = 0; j < k; ++j) {
     uint64_t key = 0;
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (j == i) key = all.v[j];
-    const bool ok = (!greedy || i == 0) && key != 0;
-    cand_tok[(long)row * k + i] = ok ? (int32_t)key_index(key) : -1;
-    cand_lp[(long)row * k + i] = ok ? (greedy ? 0.f : key_value(key) - L) : -INFINITY;
+    for (int q = 0; q < KMAX; ++q)
+      if (q == j) key = all.v[q];
+    const bool ok = (!greedy || j == 0) && key != 0;
+    cand_tok[(long)row * k + j] = ok ? (int32_t)key_index(key) : -1;
+    cand_lp[(long)row * k + j] = ok ? (greedy ? 0.f : key_value(key) - L) : -INFINITY;
   }
 }
 
@@ -71,8 +94,8 @@ hipError_t launch_merge(const float2* ms_part, const uint64_t* key_part, int row
                         int kt, int k, int kmax, int greedy, int32_t* cand_tok, float* cand_lp,
                         float* lse, hipStream_t st) {
 #define DT_MERGE(KM)                                                                        \
-  hipLaunchKernelGGL(k_merge<KM>, dim3(rows), dim3(256), 0, st, ms_part, key_part, ntiles, kt, \
-                     k, greedy, cand_tok, cand_lp, lse)
+  hipLaunchKernelGGL(k_merge<KM>, dim3(rows), dim3(MERGE_THREADS), 0, st, ms_part, key_part,   \
+                     ntiles, kt, k, greedy, cand_tok, cand_lp, lse)
   switch (kmax) {
     case 1: DT_MERGE(1); break;
     case 4: DT_MERGE(4); break;
@@ -88,34 +111,22 @@ hipError_t launch_merge(const float2* ms_part, const uint64_t* key_part, int row
 // beam bookkeeping
 // ----------------------------------------------------------------------------
 // Depth-0 frontier: row r*W of request r holds the root (token root_tok[r],
-// score 0, state row r of s0); every other row is empty.  With a bf16 head it
-// also forms x for depth 1 (grid covers max(Mp, Mp * d / 8) threads).
+// score 0, state row r of s0); every other row is empty.
 __global__ void k_beam_init(int R, int W, int Mp, const int32_t* __restrict__ root_tok,
-                            int32_t* tok, float* score, int32_t* src, PrepArgs prep) {
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+                            int32_t* tok, float* score, int32_t* src) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < Mp) {
     const bool root = i < R * W && i % W == 0;
     tok[i] = root ? root_tok[i / W] : -1;
     score[i] = root ? 0.f : -INFINITY;
-    src[i] = root ? (int)(i / W) : -1;
-  }
-  if (prep.hi) {
-    const int d8 = prep.d / 8;
-    if (i < (long)Mp * d8) {
-      const int m = i / d8, k = (i % d8) * 8;
-      const bool root = m < R * W && m % W == 0;
-      prep_x_row8(prep, m, k, root ? root_tok[m / W] : -1);
-    }
+    src[i] = root ? i / W : -1;
   }
 }
 
 hipError_t launch_beam_init(int R, int W, int Mp, const int32_t* root_tok, int32_t* tok,
-                            float* score, int32_t* src, const PrepArgs* prep, hipStream_t st) {
-  PrepArgs p;
-  if (prep) p = *prep;
-  const long n = prep ? (long)Mp * (prep->d / 8) : Mp;
-  hipLaunchKernelGGL(k_beam_init, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, R, W, Mp,
-                     root_tok, tok, score, src, p);
+                            float* score, int32_t* src, hipStream_t st) {
+  hipLaunchKernelGGL(k_beam_init, dim3((Mp + 255) / 256), dim3(256), 0, st, R, W, Mp, root_tok,
+                     tok, score, src);
   return hipGetLastError();
 }
 
@@ -141,24 +152,21 @@ hipError_t launch_fill_rows(int rows, int Mp, const int32_t* tok_in, int32_t* to
 // scores score_in[i] + cand_lp[i][rank]; the n_t = min(W, n_{t-1} keff) best
 // by (score desc, c asc) take slots 0..n_t-1 in that order.  A candidate's
 // rank is the number of candidates with a larger key (keys are distinct).
-// With a bf16 head the workgroup then forms x = E[tok] + h_{t+1} for its rows.
 constexpr int BEAM_THREADS = 1024;
 
 __global__ __launch_bounds__(BEAM_THREADS) void k_beam_select(BeamArgs b) {
-  extern __shared__ uint64_t keys[];              // [ncand], then [W] slot tokens
+  extern __shared__ uint64_t keys[];              // [ncand]
   const int r = blockIdx.x, tid = threadIdx.x;
   const int base = r * b.W;
   const int n_prev = b.t == 0 ? 1 : b.n_valid[r * b.D + b.t - 1];
   const int keff = b.greedy ? 1 : b.k;
   const int ncand = n_prev * keff;
   const int nkeep = min(b.W, ncand);
-  int32_t* slot_tok = (int32_t*)(keys + b.W * keff);
   for (int c = tid; c < ncand; c += BEAM_THREADS) {
     const int i = c / keff, rk = c % keff;
     const float sc = b.score_in[base + i] + b.cand_lp[(long)(base + i) * b.k + rk];
     keys[c] = make_key(sc, (uint32_t)c);
   }
-  for (int j = tid; j < b.W; j += BEAM_THREADS) slot_tok[j] = -1;
   __syncthreads();
   const long pool = ((long)r * b.D + b.t) * b.W;
   for (int c = tid; c < ncand; c += BEAM_THREADS) {
@@ -175,7 +183,6 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_select(BeamArgs b) {
       b.tok_out[base + rank] = tk;
       b.score_out[base + rank] = sc;
       b.src_out[base + rank] = base + i;
-      slot_tok[rank] = tk;
     }
   }
   for (int j = nkeep + tid; j < b.W; j += BEAM_THREADS) {
@@ -194,19 +201,11 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_select(BeamArgs b) {
       b.score_out[j] = -INFINITY;
       b.src_out[j] = -1;
     }
-  if (b.prep.hi) {
-    __syncthreads();
-    const int d8 = b.prep.d / 8;
-    for (int g = tid; g < b.W * d8; g += BEAM_THREADS) {
-      const int j = g / d8, k = (g % d8) * 8;
-      prep_x_row8(b.prep, base + j, k, slot_tok[j]);
-    }
-  }
 }
 
 hipError_t launch_beam_select(const BeamArgs& b, hipStream_t st) {
   const int ncand_max = b.W * (b.greedy ? 1 : b.k);
-  const size_t lds = (size_t)ncand_max * sizeof(uint64_t) + (size_t)b.W * sizeof(int32_t);
+  const size_t lds = (size_t)ncand_max * sizeof(uint64_t);
   hipLaunchKernelGGL(k_beam_select, dim3(b.R), dim3(BEAM_THREADS), lds, st, b);
   return hipGetLastError();
 }
@@ -228,15 +227,14 @@ __global__ __launch_bounds__(PRUNE_THREADS) void k_prune(
   const int P = D * W;
   uint64_t* keys = (uint64_t*)sm;                    // [P]; 0 = invalid node
   int32_t* emit = (int32_t*)(keys + P);              // [P]; emitted index or -1
-  __shared__ int total;
-  if (tid == 0) {
-    int s = 0;
-    for (int t = 0; t < D; ++t) s += n_valid[r * D + t];
-    total = s;
-  }
+  __shared__ int nv[DT_MAX_DEPTH];
+  if (tid < D) nv[tid] = n_valid[r * D + tid];
+  __syncthreads();
+  int total = 0;
+  for (int t = 0; t < D; ++t) total += nv[t];
   for (int f = tid; f < P; f += PRUNE_THREADS) {
     const int t = f / W, j = f % W;
-    const bool valid = j < n_valid[r * D + t];
+    const bool valid = j < nv[t];
     const float pr = pool_score[(long)r * P + f] + beta * (float)(t + 1);
     keys[f] = valid ? make_key(pr, (uint32_t)f) : 0ull;
   }
