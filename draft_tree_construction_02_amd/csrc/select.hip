@@ -235,7 +235,8 @@ __global__ __launch_bounds__(PRUNE_THREADS) void k_prune(
   for (int f = tid; f < P; f += PRUNE_THREADS) {
     const int t = f / W, j = f % W;
     const bool valid = j < nv[t];
-    const float pr = pool_score[(long)r * P + f] + beta * (float)(t + 1);
+    // two roundings (no contraction into an fma), as documented
+    const float pr = __fadd_rn(pool_score[(long)r * P + f], __fmul_rn(beta, (float)(t + 1)));
     keys[f] = valid ? make_key(pr, (uint32_t)f) : 0ull;
   }
   __syncthreads();
