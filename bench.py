@@ -36,6 +36,28 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def profiled_traffic(workload):
+    """HBM bytes per head launch from the committed rocprofv3 counter summary
+    (profiles/head_bf16_<workload>.md), or None when absent or when the
+    kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"head_bf16_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_launch", "source_sha256",
+                                                     "sources"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    if len(fields) != 3:
+        return None
+    h = hashlib.sha256()
+    for f in fields["sources"].split(", "):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return int(fields["traffic_bytes_per_launch"]) if h.hexdigest() == fields["source_sha256"] else None
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,7 +203,8 @@ def main():
                    "verify_layer": dict(VERIFY, n_tree=B)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "corrected-logit head (k_head_bf16)",
+                     "traffic": profiled_traffic(wl.name),
+                     "kernel": "corrected-logit head (k_head_bf16)",
                      "bytes_per_launch": head_bytes},
         "kernels_us": {n: (round(v["avg_us"], 2) if v["avg_us"] else None) for n, v in kern.items()},
         "weight_bytes_per_step": bytes_per_step,
