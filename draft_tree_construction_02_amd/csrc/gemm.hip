@@ -54,8 +54,18 @@ namespace dt {
 #ifndef DT_KC_B
 #define DT_KC_B 128
 #endif
+// Wave priority schedule of the bf16 mainloop: 0 = none; 1 = priority falls
+// from 3 to 0 as the wave progresses through its K range; 2 = priority 3 until
+// the first iteration's data arrived, then 1.  Waves of one CU are otherwise
+// served oldest first, which starves the last-dispatched workgroups.
+#ifndef DT_PRIO
+#define DT_PRIO 1
+#endif
 // 1: each wave reads its activation blocks straight from L2 (no LDS staging,
 // no barrier in the K loop); 0: the workgroup stages them once in LDS.
+#ifndef DT_AFIRST
+#define DT_AFIRST 1
+#endif
 #ifndef DT_DIRECT_A
 #define DT_DIRECT_A 0
 #endif
@@ -68,6 +78,21 @@ constexpr int KC_B = DT_KC_B;         // K staged per LDS chunk (bf16 path)
 constexpr int KC_F = 32;              // K staged per LDS chunk (fp32 path)
 constexpr int CPAD = 4;               // C tile row padding (floats)
 constexpr int BLK = 512;              // bf16 elements per packed block (1 KB)
+
+#ifdef DT_TRACE
+// per-workgroup timestamps of the bf16 mainloop (experimental builds only)
+__device__ unsigned long long g_trace[4 * 16384];
+__device__ __forceinline__ void trace_mark(int slot) {
+  const int wg = blockIdx.x + gridDim.x * blockIdx.y;
+  if (threadIdx.x == 0 && wg < 16384) g_trace[4 * wg + slot] = __builtin_amdgcn_s_memrealtime();
+}
+extern "C" int dt_trace_read(void* host, size_t bytes) {
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_trace), bytes) == hipSuccess ? 0 : -4;
+}
+#define DT_MARK(s) trace_mark(s)
+#else
+#define DT_MARK(s)
+#endif
 
 int gemm_tile_n(int w_bf16) { return w_bf16 ? TN_GEMM : TN_F; }
 int head_tile_n(int w_bf16) { return w_bf16 ? TN_HEAD : TN_F; }
@@ -257,13 +282,25 @@ __device__ __forceinline__ void tile_bf16(const ASource& a, const uint16_t* __re
   } else {
     // no register prefetch: weights and the activation chunk of iteration s
     // are requested together; other resident waves cover the latency
+    DT_MARK(0);
+    if (DT_PRIO != 0) __builtin_amdgcn_s_setprio(3);
     for (int s = 0; s < nst; ++s) {
       const int k = k0 + s * C::KC;
+      if (s == 1) DT_MARK(1);
+      if (DT_PRIO == 1) {
+        const int pr = 3 - (4 * s) / nst;
+        if (pr == 2) __builtin_amdgcn_s_setprio(2);
+        else if (pr == 1) __builtin_amdgcn_s_setprio(1);
+        else if (pr == 0) __builtin_amdgcn_s_setprio(0);
+      } else if (DT_PRIO == 2 && s == 1) {
+        __builtin_amdgcn_s_setprio(1);
+      }
       uint16_t* Ab = As + (NBUF == 2 ? (s & 1) * C::ABUF : 0);
       u32x4 b[IPS][NW][4];
+      if (DT_AFIRST) st.issue(a, k);
 #pragma unroll
       for (int it = 0; it < IPS; ++it) load_b<NW, PW>(b[it], Wt, a.K, col0, N, k + 128 * it, lane);
-      st.issue(a, k);
+      if (!DT_AFIRST) st.issue(a, k);
       if (NBUF == 1 && s > 0) __syncthreads();
       st.commit(Ab);
       __syncthreads();
@@ -271,6 +308,7 @@ __device__ __forceinline__ void tile_bf16(const ASource& a, const uint16_t* __re
       for (int it = 0; it < IPS; ++it) mma_iter<MT, C::KC, NW>(Ab, it, b[it], acc, lane);
     }
     __syncthreads();
+    DT_MARK(2);
   }
 }
 
@@ -397,6 +435,7 @@ __global__ __launch_bounds__(64 * DT_WV_GEMM) void k_gemm_bf16(GemmArgs g) {
       *(float4*)(g.part + ((long)split * Mp + m) * g.N + n) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
+  DT_MARK(3);
 }
 
 template <int MT, bool GATHER>
@@ -500,8 +539,12 @@ __device__ __forceinline__ void head_epilogue(const HeadArgs& p, const float* Cs
   }
 }
 
+#ifndef DT_HEAD_WPE
+#define DT_HEAD_WPE 1
+#endif
 template <int MT, int NBUF, int KMAX, bool PW>
-__global__ __launch_bounds__(64 * DT_WV_HEAD) void k_head_bf16(HeadArgs p) {
+__global__ __launch_bounds__(64 * DT_WV_HEAD)
+__attribute__((amdgpu_waves_per_eu(DT_HEAD_WPE, 8))) void k_head_bf16(HeadArgs p) {
   constexpr int NW = DT_NW_HEAD;
   constexpr int TN = TN_HEAD;
   __shared__ __attribute__((aligned(16))) unsigned char smem[BfCfg<MT, NBUF, NW, DT_WV_HEAD>::LDS];
@@ -525,6 +568,7 @@ __global__ __launch_bounds__(64 * DT_WV_HEAD) void k_head_bf16(HeadArgs p) {
     }
   __syncthreads();
   head_epilogue<MT, KMAX, TN, 64 * DT_WV_HEAD>(p, Cs, tile);
+  DT_MARK(3);
 }
 
 template <int MT, int KMAX>
@@ -539,12 +583,18 @@ __global__ __launch_bounds__(NT) void k_head_f32(HeadArgs p) {
 // ----------------------------------------------------------------------------
 // host launchers
 // ----------------------------------------------------------------------------
+// LDS buffers of the activation chunk: double-buffered below DT_NBUF1_MT row
+// tiles, single-buffered from there (keeps enough workgroups resident).
+#ifndef DT_NBUF1_MT
+#define DT_NBUF1_MT 8
+#endif
+
 template <int MT>
 static hipError_t gemm_mt(const GemmArgs& g, hipStream_t st) {
   const int TN = g.w_bf16 ? TN_GEMM : TN_F;
   dim3 grid((g.N + TN - 1) / TN, g.splits);
   if (g.w_bf16) {
-    constexpr int NB = MT >= 8 ? 1 : 2;
+    constexpr int NB = MT >= DT_NBUF1_MT ? 1 : 2;
     const dim3 blk(64 * DT_WV_GEMM);
     if (g.w_packed)
       hipLaunchKernelGGL((k_gemm_bf16<MT, NB, true>), grid, blk, 0, st, g);
@@ -574,7 +624,7 @@ static hipError_t head_mk(const HeadArgs& p, hipStream_t st) {
   const int TN = p.w_bf16 ? TN_HEAD : TN_F;
   dim3 grid((p.V + TN - 1) / TN);
   if (p.w_bf16) {
-    constexpr int NB = MT >= 8 ? 1 : 2;
+    constexpr int NB = MT >= DT_NBUF1_MT ? 1 : 2;
     if (p.w_packed)
       hipLaunchKernelGGL((k_head_bf16<MT, NB, KMAX, true>), grid, dim3(64 * DT_WV_HEAD), 0, st, p);
     else
