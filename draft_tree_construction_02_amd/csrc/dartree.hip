@@ -470,7 +470,7 @@ int corrected_topk(const dt_head* head, const float* s, int rows, int k, float T
 size_t pack_head_bytes(const dt_head* head) {
   if (!head_ok(head) || head->wdtype != DT_BF16) return 0;
   const size_t d = head->d, V = head->V;
-  const size_t vpad = (V + 15) / 16 * 16;
+  const size_t vpad = (V + PACK_ROWS - 1) / PACK_ROWS * PACK_ROWS;
   return align_up(4 * d * d * 2) * 2 + align_up(vpad * d * 2);
 }
 

@@ -5,10 +5,11 @@
 // is the weight stream from HBM, read exactly once per call.
 //
 // bf16 path.  Weights are streamed in the packed block layout (1 KB blocks of
-// 16 rows x 32 K in MFMA operand order, see pack.hip) with non-temporal
-// 16-byte loads, so every wave load instruction reads one contiguous 1 KB
-// block; row-major weights are also accepted (16 rows x 64 B per
-// instruction).  Activations arrive as packed hi/lo bf16 planes (hi = bf16(a),
+// 16 rows x 32 K in MFMA operand order, the 8 tiles of a 128-row group
+// interleaved per 32-K step, see pack.hip) with non-temporal 16-byte loads, so
+// every wave load instruction reads one contiguous 1 KB block and a
+// workgroup's loads of one K step form one 8 KB run; row-major weights are
+// also accepted (16 rows x 64 B per instruction).  Activations arrive as packed hi/lo bf16 planes (hi = bf16(a),
 // lo = bf16(a - hi)), written by the producing kernel; both halves go through
 // v_mfma_f32_16x16x32_bf16 with fp32 accumulation, carrying ~16 significant
 // bits of A (bf16 weights are exact).  A workgroup (4 waves) owns 128 output
@@ -148,10 +149,13 @@ __device__ __forceinline__ void load_b(u32x4 (&b)[NW][4], const uint16_t* __rest
     const int nt = col0 + 16 * c;            // first row of this column tile
     if (PACKED) {
       if (nt < N) {
-        const u32x4* p = (const u32x4*)(Wt + ((long)(nt / 16) * (K / 32) + kb / 32) * BLK +
-                                        lane * 8);
+        // grouped block order: block (g, kb, t) of tile t of row group g
+        constexpr int TPG = PACK_ROWS / 16;
+        const int tile = nt / 16;
+        const u32x4* p = (const u32x4*)(Wt + (((long)(tile / TPG) * (K / 32) + kb / 32) * TPG +
+                                              tile % TPG) * BLK + lane * 8);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[c][j] = __builtin_nontemporal_load(p + j * (BLK / 8));
+        for (int j = 0; j < 4; ++j) b[c][j] = __builtin_nontemporal_load(p + j * (TPG * BLK / 8));
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) b[c][j] = u32x4{0u, 0u, 0u, 0u};

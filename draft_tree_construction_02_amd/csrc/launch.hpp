@@ -7,6 +7,12 @@
 
 namespace dt {
 
+// Packed bf16 weights (pack_head): rows are grouped by PACK_ROWS (8 tiles of
+// 16); block (g, kb, t) of tile t, K block kb of group g sits at element
+// offset ((g * K/32 + kb) * 8 + t) * 512, so the 8 tiles of a 128-column
+// workgroup are read as one contiguous 8 KB run per 32-K step.
+constexpr int PACK_ROWS = 128;
+
 // fp32 activation source (fp32 heads): row m, column k of A.
 //   dense:  A[m][k] = a[m * lda + k]
 //   gather: A[m][k] = E[tok[m]][k] + h[(m / rpr) * h_req_stride + k]

@@ -6,25 +6,31 @@
 
 namespace dt {
 
-// One thread per 16 bytes of the packed output: block (nb, kb), lane l holds
-// row 16 nb + l % 16, K 32 kb + 8 (l / 16) .. + 8; rows >= N are zero.
+// One thread per 16 bytes of the packed output.  Rows are grouped by 128
+// (8 tiles of 16); block (g, kb, t) holds rows 128 g + 16 t .. + 15 and K
+// 32 kb .. + 31, and inside it lane l holds row 128 g + 16 t + l % 16, K
+// 32 kb + 8 (l / 16) .. + 8.  Rows >= N are zero.
 __global__ __launch_bounds__(256) void k_pack_weight(const uint16_t* __restrict__ src,
                                                      uint16_t* __restrict__ dst, int N, int K) {
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const int kblocks = K / 32;
-  const long nchunks = (long)((N + 15) / 16) * kblocks * 64;
+  const long nchunks = (long)((N + PACK_ROWS - 1) / PACK_ROWS) * (PACK_ROWS / 16) * kblocks * 64;
   if (gid >= nchunks) return;
   const int lane = gid & 63;
   const long blk = gid >> 6;
-  const int nb = blk / kblocks, kb = blk % kblocks;
-  const int n = nb * 16 + (lane & 15), k = kb * 32 + (lane >> 4) * 8;
+  const int t = blk % (PACK_ROWS / 16);
+  const long rest = blk / (PACK_ROWS / 16);
+  const int kb = rest % kblocks;
+  const long g = rest / kblocks;
+  const long n = g * PACK_ROWS + t * 16 + (lane & 15);
+  const int k = kb * 32 + (lane >> 4) * 8;
   u32x4 v = u32x4{0u, 0u, 0u, 0u};
-  if (n < N) v = *(const u32x4*)(src + (long)n * K + k);
+  if (n < N) v = *(const u32x4*)(src + n * K + k);
   *(u32x4*)(dst + gid * 8) = v;
 }
 
 hipError_t launch_pack_weight(const uint16_t* src, uint16_t* dst, int N, int K, hipStream_t st) {
-  const long n = (long)((N + 15) / 16) * (K / 32) * 64;
+  const long n = (long)((N + PACK_ROWS - 1) / PACK_ROWS) * (PACK_ROWS / 16) * (K / 32) * 64;
   hipLaunchKernelGGL(k_pack_weight, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, dst,
                      N, K);
   return hipGetLastError();

@@ -108,11 +108,13 @@ size_t pack_head_bytes(const dt_head* head);
  * packed block layout, and fill `*packed` (host struct) with a head that
  * points there (E still points to the caller's row-major E).
  * Packed layout of a matrix [N][K]: rows padded with zeros to a multiple of
- * 16; 1 KB blocks of 16 rows x 32 columns, block (nb, kb) at element offset
- * (nb * K/32 + kb) * 512; inside a block, the 8 bf16 at offset 8 l hold row
- * 16 nb + (l mod 16), columns 32 kb + 8 (l / 16) .. + 7 (l = 0..63).  This is
- * the operand order of the gfx950 bf16 MFMA, so one wave load instruction
- * streams one contiguous block.  Asynchronous on `stream`; `dst` must stay
+ * 128 and split into groups g of 128 rows, each of 8 tiles t of 16 rows;
+ * 1 KB blocks of 16 rows x 32 columns, block (g, kb, t) at element offset
+ * ((g * K/32 + kb) * 8 + t) * 512; inside a block, the 8 bf16 at offset 8 l
+ * hold row 128 g + 16 t + (l mod 16), columns 32 kb + 8 (l / 16) .. + 7
+ * (l = 0..63).  This is the operand order of the gfx950 bf16 MFMA, so one
+ * wave load instruction streams one contiguous block, and the 8 tiles of a
+ * row group advance through K as one contiguous run.  Asynchronous on `stream`; `dst` must stay
  * alive while the packed head is used.
  */
 int pack_head(const dt_head* src, void* dst, size_t dst_bytes, dt_head* packed, void* stream);

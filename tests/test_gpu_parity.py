@@ -105,10 +105,11 @@ def test_packed_layout_is_the_documented_block_order():
     off = 0
     for name, N, K in (("W1t", 4 * d, d), ("W2t", d, 4 * d), ("Ut", V, d)):
         src = getattr(hw, name)
-        Np = (N + 15) // 16 * 16
+        Np = (N + 127) // 128 * 128
         pad = np.zeros((Np, K), np.uint16)
         pad[:N] = src
-        blocks = pad.reshape(Np // 16, 16, K // 32, 4, 8).transpose(0, 2, 3, 1, 4)
+        # (group, tile, row, K block, lane group, element) -> block (group, K block, tile)
+        blocks = pad.reshape(Np // 128, 8, 16, K // 32, 4, 8).transpose(0, 3, 1, 4, 2, 5)
         got = buf[off:off + Np * K]
         assert np.array_equal(got, blocks.reshape(-1)), name
         off += (Np * K * 2 + 255) // 256 * 256 // 2
