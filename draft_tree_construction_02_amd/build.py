@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libdartree.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["dartree.hip", "gemm.hip", "select.hip", "pack.hip", "attention.hip"]
+SOURCES = ["dartree.hip", "gemm.hip", "head_wide.hip", "select.hip", "pack.hip", "attention.hip"]
 ARCH = os.environ.get("DARTREE_ARCH", "gfx950")
 
 FLAGS = [

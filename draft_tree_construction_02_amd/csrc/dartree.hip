@@ -308,7 +308,7 @@ hipError_t run_head(const dt_head* hd, const StepWs& w, const float* s, int rows
   hipError_t e = timed(DT_K_HEAD, st, [&] { return launch_head(p, st); });
   if (e != hipSuccess) return e;
   return timed(DT_K_MERGE, st, [&] {
-    return launch_merge(w.ms_part, w.key_part, rows, w.tilesV, p.k, k, p.kmax, greedy,
+    return launch_merge(w.ms_part, w.key_part, rows, head_tiles(p), p.k, k, p.kmax, greedy,
                         cand_tok, cand_lp, lse, st);
   });
 }

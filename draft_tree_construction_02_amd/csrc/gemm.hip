@@ -97,6 +97,10 @@ extern "C" int dt_trace_read(void* host, size_t bytes) {
 
 int gemm_tile_n(int w_bf16) { return w_bf16 ? TN_GEMM : TN_F; }
 int head_tile_n(int w_bf16) { return w_bf16 ? TN_HEAD : TN_F; }
+int head_tiles(const HeadArgs& p) {
+  const int tn = head_wide_ok(p) ? head_wide_tile_n() : head_tile_n(p.w_bf16);
+  return (p.V + tn - 1) / tn;
+}
 int gemm_k_chunk(int w_bf16) { return w_bf16 ? KC_B : KC_F; }
 
 __device__ __forceinline__ float gelu_f(float y) {
@@ -651,6 +655,7 @@ static hipError_t head_mt(const HeadArgs& p, hipStream_t st) {
 }
 
 hipError_t launch_head(const HeadArgs& p, hipStream_t st) {
+  if (head_wide_ok(p)) return launch_head_wide(p, st);
   switch (p.Mp) {
     case 16: return head_mt<1>(p, st);
     case 32: return head_mt<2>(p, st);

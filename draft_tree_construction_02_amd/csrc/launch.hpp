@@ -92,8 +92,13 @@ struct HeadArgs {
   float2* ms_part = nullptr;  // [Mp][ntiles]
   uint64_t* key_part = nullptr;  // [Mp][ntiles][k]
 };
-int head_tile_n(int w_bf16);
+int head_tile_n(int w_bf16);                 // smallest slice width (sizes workspaces)
+int head_tiles(const HeadArgs& h);           // vocabulary slices of this launch
 hipError_t launch_head(const HeadArgs& h, hipStream_t st);
+// 64/128-row packed bf16 variant (head_wide.hip); launch_head dispatches to it
+bool head_wide_ok(const HeadArgs& h);
+int head_wide_tile_n();
+hipError_t launch_head_wide(const HeadArgs& h, hipStream_t st);
 
 // Per-row merge of the head's tile partials (kt keys per tile): log-sum-exp
 // and global top-k, written to cand_tok / cand_lp rows of stride k.
