@@ -85,6 +85,8 @@ struct StepWs {
   uint16_t *s_hi, *s_lo;       // [Mp][d] packed (bf16 heads)
   float2* ms_part;
   uint64_t* key_part;
+  float2* ms2;                 // merge range results [Mp][MERGE_SPLITS_MAX]
+  uint64_t* key2;
   int32_t* cand_tok;
   float* cand_lp;
   float* lse;
@@ -122,6 +124,8 @@ StepWs carve_step(Carver& c, const dt_head* h, int rows, int k) {
   }
   w.ms_part = c.take<float2>((size_t)w.Mp * w.tilesV);
   w.key_part = c.take<uint64_t>((size_t)w.Mp * w.tilesV * k);
+  w.ms2 = c.take<float2>((size_t)w.Mp * MERGE_SPLITS_MAX);
+  w.key2 = c.take<uint64_t>((size_t)w.Mp * MERGE_SPLITS_MAX * kmax_for(k, false));
   w.cand_tok = c.take<int32_t>((size_t)w.Mp * k);
   w.cand_lp = c.take<float>((size_t)w.Mp * k);
   w.lse = c.take<float>(w.Mp);
@@ -285,8 +289,20 @@ hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hip
 
 // Head + merge over `rows` states; bf16 heads read s' from w.s_* (packed),
 // fp32 heads from the dense fp32 rows s.
+// Vocabulary slices of the head launch for Mp rows.
+int head_tiles_for(const dt_head* hd, int Mp) {
+  HeadArgs p;
+  p.w_bf16 = hd->wdtype == DT_BF16;
+  p.w_packed = hd->layout == DT_LAYOUT_PACKED;
+  p.V = hd->V;
+  p.d = hd->d;
+  p.Mp = Mp;
+  return head_tiles(p);
+}
+
 hipError_t run_head(const dt_head* hd, const StepWs& w, const float* s, int rows, int k, float T,
-                    int32_t* cand_tok, float* cand_lp, float* lse, hipStream_t st) {
+                    int32_t* cand_tok, float* cand_lp, float* lse, hipStream_t st,
+                    bool final_merge = true) {
   const bool greedy = T == 0.f;
   HeadArgs p;
   p.pa = PackedA{w.s_hi, w.s_lo, hd->d};
@@ -307,9 +323,14 @@ hipError_t run_head(const dt_head* hd, const StepWs& w, const float* s, int rows
   p.key_part = w.key_part;
   hipError_t e = timed(DT_K_HEAD, st, [&] { return launch_head(p, st); });
   if (e != hipSuccess) return e;
+  if (!final_merge)
+    return timed(DT_K_MERGE, st, [&] {
+      return launch_merge_part(w.ms_part, w.key_part, rows, head_tiles(p), p.k, p.kmax, w.ms2,
+                               w.key2, st);
+    });
   return timed(DT_K_MERGE, st, [&] {
     return launch_merge(w.ms_part, w.key_part, rows, head_tiles(p), p.k, k, p.kmax, greedy,
-                        cand_tok, cand_lp, lse, st);
+                        w.ms2, w.key2, cand_tok, cand_lp, lse, st);
   });
 }
 
@@ -379,12 +400,14 @@ int build_supertree(const dt_head* head, const float* h, const float* s0, const 
     io.rows_out = rows;
     e = run_update(head, w, io, st);
     if (e != hipSuccess) break;
-    e = run_head(head, w, w.S[cur], rows, k, T, w.cand_tok, w.cand_lp, w.lse, st);
+    e = run_head(head, w, w.S[cur], rows, k, T, w.cand_tok, w.cand_lp, w.lse, st, false);
     if (e != hipSuccess) break;
     BeamArgs b;
     b.R = R; b.W = W; b.k = k; b.D = D; b.t = t; b.greedy = greedy;
-    b.cand_tok = w.cand_tok;
-    b.cand_lp = w.cand_lp;
+    b.ms2 = w.ms2;
+    b.key2 = w.key2;
+    b.S = merge_splits(head_tiles_for(head, w.Mp));
+    b.kmax = kmax_for(k, greedy);
     b.score_in = w.score[cur];
     b.n_valid = n_valid;
     b.pool_tok = pool_tok;
@@ -394,7 +417,7 @@ int build_supertree(const dt_head* head, const float* h, const float* s0, const 
     b.score_out = w.score[nxt];
     b.src_out = w.src[nxt];
     b.Mp = w.Mp;
-    e = timed(DT_K_MERGE, st, [&] { return launch_beam_select(b, st); });
+    e = timed(DT_K_MERGE, st, [&] { return launch_beam_step(b, st); });
   }
   return e == hipSuccess ? DT_OK : DT_EHIP;
 }

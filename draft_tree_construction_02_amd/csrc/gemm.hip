@@ -465,23 +465,36 @@ __global__ __launch_bounds__(NT) void k_gemm_f32(GemmArgs g) {
 // ----------------------------------------------------------------------------
 // split-K reduction + epilogue; writes fp32 rows and (bf16 path) packed hi/lo
 // ----------------------------------------------------------------------------
-// One thread per (row m < Mp, 8 consecutive columns).  Rows >= rows are zero.
-__global__ __launch_bounds__(256) void k_reduce(ReduceArgs r) {
+// G consecutive threads per (row m < Mp, 8 consecutive columns): thread q
+// sums splits q, q + G, ... in order, the G partial sums are added by a
+// butterfly (a fixed order), and thread 0 of the group applies the epilogue.
+// Rows >= rows are zero.
+template <int G>
+__global__ __launch_bounds__(128) void k_reduce(ReduceArgs r) {
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const int n8 = r.N / 8;
-  if (gid >= (long)r.Mp * n8) return;
-  const int m = gid / n8, n = (gid % n8) * 8;
+  const long grp = gid / G;
+  const int q = (int)(gid % G);
+  const bool live = grp < (long)r.Mp * n8;   // no early exit: the butterfly needs every lane
+  const int m = live ? (int)(grp / n8) : 0, n = live ? (int)(grp % n8) * 8 : 0;
   float y[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = 0.f;
-  if (m < r.rows) {
-#pragma unroll 8
-    for (int s = 0; s < r.splits; ++s) {
+  if (live && m < r.rows) {
+#pragma unroll 4
+    for (int s = q; s < r.splits; s += G) {
       const float* p = r.part + ((long)s * r.Mp + m) * r.N + n;
       const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
       y[0] += a.x; y[1] += a.y; y[2] += a.z; y[3] += a.w;
       y[4] += b.x; y[5] += b.y; y[6] += b.z; y[7] += b.w;
     }
+  }
+#pragma unroll
+  for (int off = 1; off < G; off <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] += __shfl_xor(y[i], off, WAVE);
+  if (!live || q != 0) return;
+  if (m < r.rows) {
     if (r.epi == EPI_GELU) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) y[i] = gelu_f(y[i]);
@@ -503,8 +516,12 @@ __global__ __launch_bounds__(256) void k_reduce(ReduceArgs r) {
 }
 
 hipError_t launch_reduce(const ReduceArgs& r, hipStream_t st) {
-  const long n = (long)r.Mp * (r.N / 8);
-  hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, r);
+  const long groups = (long)r.Mp * (r.N / 8);
+  const int G = r.splits >= 12 ? 4 : (r.splits >= 3 ? 2 : 1);
+  const unsigned blocks = (unsigned)((groups * G + 127) / 128);
+  if (G == 4) hipLaunchKernelGGL(k_reduce<4>, dim3(blocks), dim3(128), 0, st, r);
+  else if (G == 2) hipLaunchKernelGGL(k_reduce<2>, dim3(blocks), dim3(128), 0, st, r);
+  else hipLaunchKernelGGL(k_reduce<1>, dim3(blocks), dim3(128), 0, st, r);
   return hipGetLastError();
 }
 

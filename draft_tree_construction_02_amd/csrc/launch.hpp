@@ -101,10 +101,19 @@ int head_wide_tile_n();
 hipError_t launch_head_wide(const HeadArgs& h, hipStream_t st);
 
 // Per-row merge of the head's tile partials (kt keys per tile): log-sum-exp
-// and global top-k, written to cand_tok / cand_lp rows of stride k.
+// and global top-k, written to cand_tok / cand_lp rows of stride k.  ms2 and
+// key2 hold the first pass's range results ([rows][merge_splits(ntiles)] and
+// [..][kmax]).
+int merge_splits(int ntiles);
+constexpr int MERGE_SPLITS_MAX = 16;
 hipError_t launch_merge(const float2* ms_part, const uint64_t* key_part, int rows,
-                        int ntiles, int kt, int k, int kmax, int greedy, int32_t* cand_tok,
-                        float* cand_lp, float* lse, hipStream_t st);
+                        int ntiles, int kt, int k, int kmax, int greedy, float2* ms2,
+                        uint64_t* key2, int32_t* cand_tok, float* cand_lp, float* lse,
+                        hipStream_t st);
+// First pass only (the beam step folds the range results itself).
+hipError_t launch_merge_part(const float2* ms_part, const uint64_t* key_part, int rows,
+                             int ntiles, int kt, int kmax, float2* ms2, uint64_t* key2,
+                             hipStream_t st);
 
 // x = E[tok[m]] + h[(m / rpr) * h_req_stride] written as packed hi/lo planes
 // [Mp][d] (bf16 heads); rows m >= rows or with tok[m] < 0 are zero.
@@ -128,8 +137,9 @@ hipError_t launch_pack_weight(const uint16_t* src, uint16_t* dst, int N, int K, 
 // Beam bookkeeping for one depth of R requests.
 struct BeamArgs {
   int R = 0, W = 0, k = 0, D = 0, t = 0, greedy = 0;
-  const int32_t* cand_tok = nullptr;   // [R*W][k]
-  const float* cand_lp = nullptr;      // [R*W][k]
+  const float2* ms2 = nullptr;         // merge range results [Mp][S]
+  const uint64_t* key2 = nullptr;      // [Mp][S][kmax]
+  int S = 1, kmax = 1;
   const float* score_in = nullptr;     // [R*W]
   int32_t* n_valid = nullptr;          // [R][D]
   int32_t* pool_tok = nullptr;         // [R][D][W]
@@ -142,7 +152,9 @@ struct BeamArgs {
 };
 hipError_t launch_beam_init(int R, int W, int Mp, const int32_t* root_tok, int32_t* tok,
                             float* score, int32_t* src, hipStream_t st);
-hipError_t launch_beam_select(const BeamArgs& b, hipStream_t st);
+// Children of every frontier row from the merge range results, then the
+// global top-W step.
+hipError_t launch_beam_step(const BeamArgs& b, hipStream_t st);
 hipError_t launch_fill_rows(int rows, int Mp, const int32_t* tok_in, int32_t* tok,
                             int32_t* src, hipStream_t st);
 

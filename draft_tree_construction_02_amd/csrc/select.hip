@@ -10,45 +10,68 @@
 namespace dt {
 
 // ----------------------------------------------------------------------------
-// merge: one workgroup (8 waves) per row
+// merge: per row, the head's tile partials -> log-sum-exp and top-k
 // ----------------------------------------------------------------------------
-// Each thread folds up to MERGE_BATCH tiles per pass (loads issued together),
-// each wave reduces by a butterfly, then lanes 0..7 of wave 0 reduce the 8
-// wave results by another butterfly.  The (max, sum) pairs combine in the same
-// fixed tree, so the result does not depend on timing.
-constexpr int MERGE_THREADS = 512;
+// Two passes.  Pass 1: workgroup (row, s) folds the s-th of S contiguous
+// ranges of tiles: the (max, sum) pair of tile t goes to thread t % 256, the
+// range's keys (one contiguous array) are read in consecutive 16-byte pieces
+// (a wave's load covers 1 KB) and folded into per-thread register top-k
+// lists; a butterfly in each wave and one over the 4 wave results leave the
+// range's (max, sum) and top-KMAX keys.  Pass 2: one wave per row folds the
+// S range results by a butterfly and writes the row's children.  Every
+// combination follows a fixed tree, so the result does not depend on timing.
+constexpr int MERGE_THREADS = 256;
 
 template <int KMAX>
-__global__ __launch_bounds__(MERGE_THREADS) void k_merge(const float2* __restrict__ ms_part,
-                                                         const uint64_t* __restrict__ key_part,
-                                                         int ntiles, int kt, int k, int greedy,
-                                                         int32_t* __restrict__ cand_tok,
-                                                         float* __restrict__ cand_lp,
-                                                         float* __restrict__ lse) {
-  constexpr int MERGE_BATCH = KMAX >= 16 ? 2 : 4;
-  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ __launch_bounds__(MERGE_THREADS) void k_merge_part(const float2* __restrict__ ms_part,
+                                                              const uint64_t* __restrict__ key_part,
+                                                              int ntiles, int kt,
+                                                              float2* __restrict__ ms2,
+                                                              uint64_t* __restrict__ key2) {
+  constexpr int BATCH = 4;
+  const int row = blockIdx.x, s = blockIdx.y, S = gridDim.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t_lo = (int)((long)s * ntiles / S), t_hi = (int)((long)(s + 1) * ntiles / S);
   MaxSum ms{-INFINITY, 0.f};
   TopK<KMAX> tk;
   tk.clear();
   const float2* mrow = ms_part + (long)row * ntiles;
-  const uint64_t* krow = key_part + (long)row * ntiles * kt;
-  for (int t0 = 0; t0 < ntiles; t0 += MERGE_THREADS * MERGE_BATCH) {
-    float2 p[MERGE_BATCH];
-    uint64_t kv[MERGE_BATCH][KMAX];
+  for (int t0 = t_lo; t0 < t_hi; t0 += MERGE_THREADS * BATCH) {
+    float2 p[BATCH];
 #pragma unroll
-    for (int b = 0; b < MERGE_BATCH; ++b) {
+    for (int b = 0; b < BATCH; ++b) {
       const int t = t0 + b * MERGE_THREADS + tid;
-      p[b] = t < ntiles ? mrow[t] : make_float2(-INFINITY, 0.f);
-#pragma unroll
-      for (int i = 0; i < KMAX; ++i) kv[b][i] = (t < ntiles && i < kt) ? krow[(long)t * kt + i] : 0ull;
+      p[b] = t < t_hi ? mrow[t] : make_float2(-INFINITY, 0.f);
     }
 #pragma unroll
-    for (int b = 0; b < MERGE_BATCH; ++b) {
-      ms.combine(p[b].x, p[b].y);
+    for (int b = 0; b < BATCH; ++b) ms.combine(p[b].x, p[b].y);
+  }
+  // keys of the range: words [w_lo, w_hi) of the row's array, read as
+  // aligned pairs where possible
+  const uint64_t* krow = key_part + (long)row * ntiles * kt;
+  long w_lo = (long)t_lo * kt;
+  const long w_hi = (long)t_hi * kt;
+  if (((uintptr_t)(krow + w_lo) & 15) != 0 && w_lo < w_hi) {
+    if (tid == 0) tk.insert(krow[w_lo]);
+    ++w_lo;
+  }
+  const long np = (w_hi - w_lo) / 2;
+  const ulonglong2* kp = (const ulonglong2*)(krow + w_lo);
+  for (long f0 = 0; f0 < np; f0 += MERGE_THREADS * BATCH) {
+    ulonglong2 v[BATCH];
 #pragma unroll
-      for (int i = 0; i < KMAX; ++i) tk.insert(kv[b][i]);
+    for (int b = 0; b < BATCH; ++b) {
+      const long f = f0 + b * MERGE_THREADS + tid;
+      v[b] = f < np ? kp[f] : make_ulonglong2(0ull, 0ull);
+    }
+#pragma unroll
+    for (int b = 0; b < BATCH; ++b) {
+      tk.insert(v[b].x);
+      tk.insert(v[b].y);
     }
   }
+  if (((w_hi - w_lo) & 1) && tid == MERGE_THREADS - 1) tk.insert(krow[w_hi - 1]);
+
   for (int off = 1; off < 64; off <<= 1) {
     const float m2 = __shfl_xor(ms.m, off, 64);
     const float s2 = __shfl_xor(ms.s, off, 64);
@@ -77,6 +100,42 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_merge(const float2* __restric
   }
   all.reduce_lanes(NWV);
   if (lane != 0) return;
+  const long o = (long)row * S + s;
+  ms2[o] = make_float2(tot.m, tot.s);
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) key2[o * KMAX + i] = all.v[i];
+}
+
+// One wave per row: lane s < S holds range s; butterfly over S2 lanes (S
+// rounded up to a power of two).
+template <int KMAX>
+__global__ __launch_bounds__(64) void k_merge_final(const float2* __restrict__ ms2,
+                                                    const uint64_t* __restrict__ key2, int S,
+                                                    int k, int greedy,
+                                                    int32_t* __restrict__ cand_tok,
+                                                    float* __restrict__ cand_lp,
+                                                    float* __restrict__ lse) {
+  const int row = blockIdx.x, lane = threadIdx.x;
+  const bool have = lane < S;
+  const long o = (long)row * S + lane;
+  MaxSum tot{-INFINITY, 0.f};
+  TopK<KMAX> all;
+  all.clear();
+  if (have) {
+    const float2 e = ms2[o];
+    tot = MaxSum{e.x, e.y};
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) all.v[i] = key2[o * KMAX + i];
+  }
+  int S2 = 1;
+  while (S2 < S) S2 <<= 1;
+  for (int off = 1; off < S2; off <<= 1) {
+    const float m2 = __shfl_xor(tot.m, off, 64);
+    const float s2 = __shfl_xor(tot.s, off, 64);
+    tot.combine(m2, s2);
+  }
+  all.reduce_lanes(S2);
+  if (lane != 0) return;
   const float L = greedy ? tot.m : tot.m + logf(tot.s);
   lse[row] = L;
   for (int j = 0; j < k; ++j) {
@@ -90,12 +149,38 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_merge(const float2* __restric
   }
 }
 
+hipError_t launch_merge_part(const float2* ms_part, const uint64_t* key_part, int rows,
+                             int ntiles, int kt, int kmax, float2* ms2, uint64_t* key2,
+                             hipStream_t st) {
+  const int S = merge_splits(ntiles);
+#define DT_MERGE1(KM)                                                                        \
+  hipLaunchKernelGGL(k_merge_part<KM>, dim3(rows, S), dim3(MERGE_THREADS), 0, st, ms_part,     \
+                     key_part, ntiles, kt, ms2, key2)
+  switch (kmax) {
+    case 1: DT_MERGE1(1); break;
+    case 4: DT_MERGE1(4); break;
+    case 8: DT_MERGE1(8); break;
+    case 16: DT_MERGE1(16); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef DT_MERGE1
+  return hipGetLastError();
+}
+
+int merge_splits(int ntiles) {
+  const int s = ntiles / 128;
+  return s < 1 ? 1 : (s > MERGE_SPLITS_MAX ? MERGE_SPLITS_MAX : s);
+}
+
 hipError_t launch_merge(const float2* ms_part, const uint64_t* key_part, int rows, int ntiles,
-                        int kt, int k, int kmax, int greedy, int32_t* cand_tok, float* cand_lp,
-                        float* lse, hipStream_t st) {
-#define DT_MERGE(KM)                                                                        \
-  hipLaunchKernelGGL(k_merge<KM>, dim3(rows), dim3(MERGE_THREADS), 0, st, ms_part, key_part,   \
-                     ntiles, kt, k, greedy, cand_tok, cand_lp, lse)
+                        int kt, int k, int kmax, int greedy, float2* ms2, uint64_t* key2,
+                        int32_t* cand_tok, float* cand_lp, float* lse, hipStream_t st) {
+  const int S = merge_splits(ntiles);
+#define DT_MERGE(KM)                                                                          \
+  hipLaunchKernelGGL(k_merge_part<KM>, dim3(rows, S), dim3(MERGE_THREADS), 0, st, ms_part,      \
+                     key_part, ntiles, kt, ms2, key2);                                          \
+  hipLaunchKernelGGL(k_merge_final<KM>, dim3(rows), dim3(64), 0, st, ms2, key2, S, k, greedy,   \
+                     cand_tok, cand_lp, lse)
   switch (kmax) {
     case 1: DT_MERGE(1); break;
     case 4: DT_MERGE(4); break;
@@ -148,24 +233,61 @@ hipError_t launch_fill_rows(int rows, int Mp, const int32_t* tok_in, int32_t* to
   return hipGetLastError();
 }
 
-// One workgroup per request.  Candidate c = i * keff + rank of frontier row i
-// scores score_in[i] + cand_lp[i][rank]; the n_t = min(W, n_{t-1} keff) best
-// by (score desc, c asc) take slots 0..n_t-1 in that order.  A candidate's
-// rank is the number of candidates with a larger key (keys are distinct).
+// One workgroup per request, two phases.
+// 1. Children of each frontier row i (one wave per row): the row's S merge
+//    range results are folded by a butterfly into (max, sum exp) and the
+//    top-keff keys; child rank j gets logp = value - log-sum-exp (0 at T=0).
+// 2. Candidate c = i * keff + j scores score_in[i] + logp; the
+//    n_t = min(W, n_{t-1} keff) best by (score desc, c asc) take slots
+//    0..n_t-1 in that order.  A candidate's slot is the number of candidates
+//    with a larger key (keys are distinct).
 constexpr int BEAM_THREADS = 1024;
 
-__global__ __launch_bounds__(BEAM_THREADS) void k_beam_select(BeamArgs b) {
-  extern __shared__ uint64_t keys[];              // [ncand]
-  const int r = blockIdx.x, tid = threadIdx.x;
+template <int KMAX>
+__global__ __launch_bounds__(BEAM_THREADS) void k_beam_step(BeamArgs b) {
+  extern __shared__ uint64_t keys[];                       // [ncand]
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int base = r * b.W;
   const int n_prev = b.t == 0 ? 1 : b.n_valid[r * b.D + b.t - 1];
   const int keff = b.greedy ? 1 : b.k;
   const int ncand = n_prev * keff;
   const int nkeep = min(b.W, ncand);
-  for (int c = tid; c < ncand; c += BEAM_THREADS) {
-    const int i = c / keff, rk = c % keff;
-    const float sc = b.score_in[base + i] + b.cand_lp[(long)(base + i) * b.k + rk];
-    keys[c] = make_key(sc, (uint32_t)c);
+  const int ncand_max = b.W * keff;
+  int32_t* c_tok = (int32_t*)(keys + ncand_max);           // [ncand]
+
+  int S2 = 1;
+  while (S2 < b.S) S2 <<= 1;
+  for (int i = wave; i < n_prev; i += BEAM_THREADS / 64) {
+    const long o = (long)(base + i) * b.S + lane;
+    MaxSum tot{-INFINITY, 0.f};
+    TopK<KMAX> all;
+    all.clear();
+    if (lane < b.S) {
+      const float2 e = b.ms2[o];
+      tot = MaxSum{e.x, e.y};
+#pragma unroll
+      for (int q = 0; q < KMAX; ++q) all.v[q] = b.key2[o * KMAX + q];
+    }
+    for (int off = 1; off < S2; off <<= 1) {
+      const float m2 = __shfl_xor(tot.m, off, 64);
+      const float s2 = __shfl_xor(tot.s, off, 64);
+      tot.combine(m2, s2);
+    }
+    all.reduce_lanes(S2);
+    if (lane == 0) {
+      const float L = b.greedy ? tot.m : tot.m + logf(tot.s);
+      const float sp = b.score_in[base + i];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < keff) {
+          const uint64_t key = all.v[j];
+          const bool ok = key != 0;
+          const float lp = ok ? (b.greedy ? 0.f : key_value(key) - L) : -INFINITY;
+          c_tok[i * keff + j] = ok ? (int32_t)key_index(key) : -1;
+          keys[i * keff + j] = make_key(sp + lp, (uint32_t)(i * keff + j));
+        }
+      }
+    }
   }
   __syncthreads();
   const long pool = ((long)r * b.D + b.t) * b.W;
@@ -174,8 +296,8 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_select(BeamArgs b) {
     int rank = 0;
     for (int j = 0; j < ncand; ++j) rank += keys[j] > kc;
     if (rank < nkeep) {
-      const int i = c / keff, rk = c % keff;
-      const int32_t tk = b.cand_tok[(long)(base + i) * b.k + rk];
+      const int i = c / keff;
+      const int32_t tk = c_tok[c];
       const float sc = key_value(kc);
       b.pool_tok[pool + rank] = tk;
       b.pool_parent[pool + rank] = b.t == 0 ? -1 : i;
@@ -203,10 +325,16 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_select(BeamArgs b) {
     }
 }
 
-hipError_t launch_beam_select(const BeamArgs& b, hipStream_t st) {
-  const int ncand_max = b.W * (b.greedy ? 1 : b.k);
-  const size_t lds = (size_t)ncand_max * sizeof(uint64_t);
-  hipLaunchKernelGGL(k_beam_select, dim3(b.R), dim3(BEAM_THREADS), lds, st, b);
+hipError_t launch_beam_step(const BeamArgs& b, hipStream_t st) {
+  const int keff = b.greedy ? 1 : b.k;
+  const size_t lds = (size_t)b.W * keff * (sizeof(uint64_t) + sizeof(int32_t));
+  switch (b.kmax) {
+    case 1: hipLaunchKernelGGL(k_beam_step<1>, dim3(b.R), dim3(BEAM_THREADS), lds, st, b); break;
+    case 4: hipLaunchKernelGGL(k_beam_step<4>, dim3(b.R), dim3(BEAM_THREADS), lds, st, b); break;
+    case 8: hipLaunchKernelGGL(k_beam_step<8>, dim3(b.R), dim3(BEAM_THREADS), lds, st, b); break;
+    case 16: hipLaunchKernelGGL(k_beam_step<16>, dim3(b.R), dim3(BEAM_THREADS), lds, st, b); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
