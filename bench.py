@@ -150,29 +150,48 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    def timed_region(per_kernel: bool):
+    def build_only():
+        A.build_supertree(head, h, s0, root, D, W, k, wl.T, workspace=ws, out=pool)
+
+    def build_prune_mask():
+        build_only()
+        A.prune_topB(pool["pool_score"], pool["pool_parent"], pool["n_valid"], B, wl.beta,
+                     out=sel)
+        A.build_tree_mask(sel["sel_parent"], sel["n_sel"], out=mask)
+
+    def timed_region(fn, per_kernel: bool):
+        # events between consecutive steps give the per-step distribution;
+        # the region's total (events and host wall clock) gives the throughput
         A.timing_reset()
         A.timing_enable(per_kernel)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
         w0 = time.perf_counter()
-        e0.record()
-        for _ in range(args.steps):
-            step()
-        e1.record()
+        ev[0].record()
+        for i in range(args.steps):
+            fn()
+            ev[i + 1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
         A.timing_enable(False)
-        return e0.elapsed_time(e1), wall
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+        return ev[0].elapsed_time(ev[-1]), wall, per
 
-    ev_ms, wall = timed_region(False)
+    def pct(v, q):
+        return v[min(len(v) - 1, int(q * len(v)))]
+
+    ev_ms, wall, per = timed_region(step, False)
     ms_per_step = max(ev_ms, wall * 1e3) / args.steps
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (events {ev_ms:.1f} ms, "
-        f"wall {wall * 1e3:.1f} ms)")
-    # the same steps again with every library launch bracketed by HIP events
-    pk_ms, _ = timed_region(True)
+        f"wall {wall * 1e3:.1f} ms; median {pct(per, 0.5):.3f}, p10 {pct(per, 0.1):.3f}, "
+        f"p90 {pct(per, 0.9):.3f} ms)")
+    # build alone, and build + prune + mask (no verification layer)
+    b_ms, b_wall, b_per = timed_region(build_only, False)
+    bpm_ms, bpm_wall, bpm_per = timed_region(build_prune_mask, False)
+    # the full steps again with every library launch bracketed by HIP events
+    pk_ms, _, _ = timed_region(step, True)
     kern = {}
-    for name in ("gemm1", "gemm2", "reduce", "head", "merge_select"):
+    for name in ("gemm1", "gemm2", "reduce", "head", "merge_select", "attention"):
         tot, n = A.timing_read(name)
         kern[name] = dict(launches=n, avg_us=(tot * 1e3 / n) if n else None)
     head_us = kern["head"]["avg_us"]
@@ -183,6 +202,12 @@ def main():
         f"per-kernel timed region {pk_ms / args.steps:.3f} ms/step")
 
     builds_per_s = R * 1e3 / ms_per_step
+    # verification layer: QK^T and PV over prefix + tree keys for every query head
+    attn_flops = 4.0 * B * (VERIFY["P"] + B) * VERIFY["hd"] * VERIFY["Hq"]
+    attn_us = kern["attention"]["avg_us"]
+    rows_p = next(m for m in (16, 32, 64, 128) if m >= R * W)   # padded batch rows
+    head_kernel = ("k_head_wide (64 columns per wave, 64/128 rows)"
+                   if wl.wdtype == "bf16" and rows_p >= 64 else "k_head_bf16")
     # weights streamed per step: U (d V) + W1 and W2 (8 d^2) per depth, shared by R requests
     bytes_per_step = D * wbytes * (wl.d * wl.V + 8 * wl.d * wl.d)
     res = {
@@ -204,8 +229,17 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": profiled_traffic(wl.name),
-                     "kernel": "corrected-logit head (k_head_bf16)",
+                     "kernel": f"corrected-logit head ({head_kernel})",
                      "bytes_per_launch": head_bytes},
+        "step_ms": {"mean": round(ms_per_step, 4), "median": round(pct(per, 0.5), 4),
+                    "p10": round(pct(per, 0.1), 4), "p90": round(pct(per, 0.9), 4)},
+        "builds_per_s_build_only": round(R * 1e3 * args.steps / max(b_ms, b_wall * 1e3), 3),
+        "builds_per_s_build_prune_mask": round(R * 1e3 * args.steps / max(bpm_ms, bpm_wall * 1e3),
+                                               3),
+        "attention": {"us": round(attn_us, 2) if attn_us else None, "flop": attn_flops,
+                      "tflops": round(attn_flops / (attn_us * 1e-6) / 1e12, 2) if attn_us else None,
+                      "frac_of_bf16_dense_peak": round(attn_flops / (attn_us * 1e-6) / 2.5e15, 4)
+                      if attn_us else None},
         "kernels_us": {n: (round(v["avg_us"], 2) if v["avg_us"] else None) for n, v in kern.items()},
         "weight_bytes_per_step": bytes_per_step,
         "step_weight_stream_gbs": round(bytes_per_step / (ms_per_step * 1e-3) / 1e9, 1),

@@ -5,24 +5,30 @@
 // workgroup (4 waves x 16 rows) owns one key/value head, 64 rows and one
 // contiguous range of keys, where keys [0, P) are the prefix (always visible)
 // and keys [P, P + n) are the tree nodes (visible where the query's ancestor
-// bitmask has the bit).  For each 32-key block the K and V tiles are staged in
-// LDS; S^T = K Q^T runs on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
-// Pass 1 finds each row's maximum over the range, pass 2 accumulates
-// l = sum exp(s - max) in fp32 and O = P V with P rounded to bf16.  A combine
-// kernel merges the key ranges: out = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s.
+// bitmask has the bit).  Keys are processed in blocks of 64 in one pass with
+// an online softmax: the next block's K and V are loaded into registers while
+// the current block, staged in LDS (K row-major, V transposed), feeds
+// S^T = K Q^T and O += P V on v_mfma_f32_16x16x32_bf16 with fp32
+// accumulation; per row the running maximum m and sum l are rescaled when m
+// grows, and P is rounded to bf16 for the PV product.  A combine kernel
+// merges the key ranges: out = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s.
 #include <cmath>
+#include <type_traits>
 
 #include "../../include/dartree.h"
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace dt {
 
 constexpr int AT_THREADS = 256;
 constexpr int AT_ROWS = 64;        // rows per workgroup (16 per wave)
-constexpr int AT_KB = 32;          // keys per block
+constexpr int AT_KB = 64;          // keys per block
 constexpr int HD = 128;
 constexpr int KLD = HD + 8;        // K tile row stride (bf16)
 constexpr int VLD = AT_KB + 8;     // transposed V tile row stride (bf16)
+constexpr int AT_CH = AT_KB * (HD / 8) / AT_THREADS;   // 16-byte chunks per thread per tile
+static_assert(AT_CH == 4 && AT_KB == 64 && AT_THREADS == 256, "staging map: 32 key pairs x 8 dim groups");
 
 struct AttnArgs {
   const uint16_t* q;
@@ -44,59 +50,67 @@ __device__ __forceinline__ const uint16_t* key_row(const AttnArgs& a, const uint
                    : tree + ((long)(key - a.P) * a.Hkv + g) * HD;
 }
 
-// Stage K [32][128] and V^T [128][32] of keys [kb, kb + 32) into LDS.
-__device__ __forceinline__ void stage_kv(const AttnArgs& a, int g, int kb, int kend,
-                                         uint16_t* Ks, uint16_t* Vts) {
-  const int tid = threadIdx.x;
-  // 32 keys x 16 chunks of 8 bf16 = 512 chunks, 2 per thread
-  for (int c = tid; c < AT_KB * (HD / 8); c += AT_THREADS) {
-    const int kk = c / (HD / 8), d8 = (c % (HD / 8)) * 8;
-    const int key = kb + kk;
-    u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
-    if (key < kend) {
-      kv = *(const u32x4*)(key_row(a, a.kp, a.kt, key, g) + d8);
-      vv = *(const u32x4*)(key_row(a, a.vp, a.vt, key, g) + d8);
-    }
-    *(u32x4*)(Ks + kk * KLD + d8) = kv;
+// This thread's share of keys [kb, kb + 64): the key pair kk = 2 (tid % 32),
+// kk + 1 and dims 16 (tid / 32) .. + 16 of K and V (keys >= kend are 0).
+// kv[2 e + h] / vv[2 e + h] hold key kk + e, dims 16 (tid / 32) + 8 h .. + 8.
+__device__ __forceinline__ void load_kv(const AttnArgs& a, int g, int kb, int kend,
+                                        u32x4 (&kv)[AT_CH], u32x4 (&vv)[AT_CH]) {
+  const int kk = 2 * (threadIdx.x % 32), d16 = 16 * (threadIdx.x / 32);
+  // every load is issued (rows past the range re-read the last key and are
+  // zeroed afterwards), so the vector-memory counter is the same on every path
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      Vts[(d8 + 2 * e) * VLD + kk] = (uint16_t)(vv[e] & 0xffffu);
-      Vts[(d8 + 2 * e + 1) * VLD + kk] = (uint16_t)(vv[e] >> 16);
+  for (int e = 0; e < 2; ++e) {
+    const int key = kb + kk + e;
+    const int kc = min(key, kend - 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      kv[2 * e + h] = *(const u32x4*)(key_row(a, a.kp, a.kt, kc, g) + d16 + 8 * h);
+      vv[2 * e + h] = *(const u32x4*)(key_row(a, a.vp, a.vt, kc, g) + d16 + 8 * h);
     }
   }
 }
 
-// S^T for 32 keys x 16 rows of this wave: st[h][r] = s(key = kb + 16 h + 4 g + r,
-// row = lane % 16), scaled; masked or missing keys are -inf.
-__device__ __forceinline__ void scores(const AttnArgs& a, const uint16_t* Ks, const u32x4 (&qf)[4],
-                                       int kb, int kend, int qi, bool row_ok, float (&st)[2][4]) {
-  const int lane = threadIdx.x & 63, r16 = lane & 15, g4 = lane >> 4;
+__device__ __forceinline__ void zero_past_end(int kb, int kend, u32x4 (&kv)[AT_CH],
+                                              u32x4 (&vv)[AT_CH]) {
+  const int kk = 2 * (threadIdx.x % 32);
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t keep = kb + kk + e < kend ? 0xffffffffu : 0u;   // select, no branch
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const u32x4 kf = *(const u32x4*)(Ks + (16 * h + r16) * KLD + kk * 32 + g4 * 8);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
-                                                    __builtin_bit_cast(bf16x8, qf[kk]), acc, 0,
-                                                    0, 0);
-    }
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = kb + 16 * h + 4 * g4 + r;
-      bool vis = row_ok && key < kend;
-      if (vis && key >= a.P) {
-        const int j = key - a.P;
-        vis = (a.mask[(long)qi * a.words + (j >> 5)] >> (j & 31)) & 1u;
+      for (int w = 0; w < 4; ++w) {
+        kv[2 * e + h][w] &= keep;
+        vv[2 * e + h][w] &= keep;
       }
-      st[h][r] = vis ? acc[r] * a.scale : -INFINITY;
-    }
   }
+}
+
+// K rows as they are; V transposed, each 32-bit write holding the pair of
+// keys (kk, kk + 1) of one dim, so a wave's writes of one dim are 32
+// consecutive words.
+__device__ __forceinline__ void store_kv(const u32x4 (&kv)[AT_CH], const u32x4 (&vv)[AT_CH],
+                                         uint16_t* Ks, uint16_t* Vts) {
+  const int kk = 2 * (threadIdx.x % 32), d16 = 16 * (threadIdx.x / 32);
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) *(u32x4*)(Ks + (kk + e) * KLD + d16 + 8 * h) = kv[2 * e + h];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t a0 = vv[h][w], a1 = vv[2 + h][w];    // keys kk, kk + 1: dims 2 w, 2 w + 1
+      const int d = d16 + 8 * h + 2 * w;
+      *(uint32_t*)(Vts + d * VLD + kk) = (a0 & 0xffffu) | (a1 << 16);
+      *(uint32_t*)(Vts + (d + 1) * VLD + kk) = (a0 >> 16) | (a1 & 0xffff0000u);
+    }
 }
 
 __global__ __launch_bounds__(AT_THREADS) void k_tree_attn(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[AT_KB * KLD];
   __shared__ __attribute__((aligned(16))) uint16_t Vts[HD * VLD];
+  __shared__ uint32_t Ms[AT_ROWS * (DT_MAX_B / 32)];      // ancestor masks of the 64 rows
   const int g = blockIdx.x, rb = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g4 = lane >> 4;
@@ -104,7 +118,7 @@ __global__ __launch_bounds__(AT_THREADS) void k_tree_attn(AttnArgs a) {
   const int kbeg = split * a.keys_per_split;
   const int kend = min(a.P + a.n, kbeg + a.keys_per_split);
 
-  // this lane's row (as the MFMA B operand / S^T column)
+  // this lane's row (the MFMA B operand of S^T and the A operand of P V)
   const int row = rb * AT_ROWS + wave * 16 + r16;
   const bool row_ok = row < nrows;
   const int qi = row_ok ? row / a.group : 0;
@@ -115,57 +129,106 @@ __global__ __launch_bounds__(AT_THREADS) void k_tree_attn(AttnArgs a) {
     qf[kk] = row_ok ? *(const u32x4*)(a.q + ((long)qi * a.Hq + qh) * HD + kk * 32 + g4 * 8)
                     : u32x4{0u, 0u, 0u, 0u};
 
-  // pass 1: row maximum over the key range
-  float mx = -INFINITY;
-  for (int kb = kbeg; kb < kend; kb += AT_KB) {
-    __syncthreads();
-    stage_kv(a, g, kb, kend, Ks, Vts);
-    __syncthreads();
-    float st[2][4];
-    scores(a, Ks, qf, kb, kend, qi, row_ok, st);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, st[h][r]);
+  for (int idx = tid; idx < AT_ROWS * a.words; idx += AT_THREADS) {
+    const int lr = idx / a.words, w = idx % a.words, rr = rb * AT_ROWS + lr;
+    Ms[lr * (DT_MAX_B / 32) + w] = rr < nrows ? a.mask[(long)(rr / a.group) * a.words + w] : 0u;
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const uint32_t* mrow = Ms + (wave * 16 + r16) * (DT_MAX_B / 32);
 
-  // pass 2: l and O relative to mx
-  float l = 0.f;
+  float m = -INFINITY, l = 0.f;
   f32x4 o[HD / 16];
 #pragma unroll
   for (int t = 0; t < HD / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kb = kbeg; kb < kend; kb += AT_KB) {
+  // two register sets: block b + 2 is requested while block b is computed
+  u32x4 kv[2][AT_CH], vv[2][AT_CH];
+  load_kv(a, g, kbeg, kend, kv[0], vv[0]);
+  load_kv(a, g, kbeg + AT_KB, kend, kv[1], vv[1]);
+  auto block = [&](int kb, auto set_tag) {
+    constexpr int SET = decltype(set_tag)::value;
+    __syncthreads();                       // every wave is done with the previous tiles
+    zero_past_end(kb, kend, kv[SET], vv[SET]);
+    store_kv(kv[SET], vv[SET], Ks, Vts);
     __syncthreads();
-    stage_kv(a, g, kb, kend, Ks, Vts);
-    __syncthreads();
-    float st[2][4];
-    scores(a, Ks, qf, kb, kend, qi, row_ok, st);
-    uint32_t pk[4];
+    load_kv(a, g, kb + 2 * AT_KB, kend, kv[SET], vv[SET]);
+
+    // S^T: st[h][r] = s(key = kb + 16 h + 4 g4 + r, row = lane % 16), scaled;
+    // masked or missing keys are -inf
+    float st[4][4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 4; ++h) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const u32x4 kf = *(const u32x4*)(Ks + (16 * h + r16) * KLD + kk * 32 + g4 * 8);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                      __builtin_bit_cast(bf16x8, qf[kk]), acc,
+                                                      0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kb + 16 * h + 4 * g4 + r;
+        bool vis = row_ok && key < kend;
+        if (vis && key >= a.P) {
+          const int j = key - a.P;
+          vis = (mrow[j >> 5] >> (j & 31)) & 1u;
+        }
+        st[h][r] = vis ? acc[r] * a.scale : -INFINITY;
+      }
+    }
+    // online softmax: block maximum of the row, rescale l and O
+    float bm = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bm = fmaxf(bm, st[h][r]);
+    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    const float mn = fmaxf(m, bm);
+    const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
+    uint32_t pk[8];
+    float ls = 0.f;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
 #pragma unroll
       for (int r = 0; r < 4; r += 2) {
-        const float p0 = mx == -INFINITY ? 0.f : expf(st[h][r] - mx);
-        const float p1 = mx == -INFINITY ? 0.f : expf(st[h][r + 1] - mx);
-        l += p0 + p1;
+        const float p0 = st[h][r] == -INFINITY ? 0.f : expf(st[h][r] - mn);
+        const float p1 = st[h][r + 1] == -INFINITY ? 0.f : expf(st[h][r + 1] - mn);
+        ls += p0 + p1;
         pk[h * 2 + r / 2] = f32_to_bf16(p0) | (f32_to_bf16(p1) << 16);
       }
-    // P as the A operand: row = lane % 16, MFMA k index 8 g4 + e <-> key
-    // 4 g4 + e (e < 4) and 16 + 4 g4 + e - 4 (e >= 4)
-    const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    l = l * alpha + ls;
+    m = mn;
+    // O rows of this lane are 4 g4 + r: their factors live in lanes 4 g4 + r
 #pragma unroll
-    for (int t = 0; t < HD / 16; ++t) {
-      const int dim = 16 * t + r16;
-      const uint2 v0 = *(const uint2*)(Vts + dim * VLD + 4 * g4);
-      const uint2 v1 = *(const uint2*)(Vts + dim * VLD + 16 + 4 * g4);
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t], 0, 0, 0);
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __shfl(alpha, 4 * g4 + r, 64);
+#pragma unroll
+      for (int t = 0; t < HD / 16; ++t) o[t][r] *= ar;
     }
+    // P as the A operand, 32 keys per MFMA: k index 8 g4 + e <-> key
+    // 32 q + 4 g4 + e (e < 4) and 32 q + 16 + 4 g4 + e - 4 (e >= 4)
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const bf16x8 pa = __builtin_bit_cast(
+          bf16x8, u32x4{pk[4 * qq], pk[4 * qq + 1], pk[4 * qq + 2], pk[4 * qq + 3]});
+#pragma unroll
+      for (int t = 0; t < HD / 16; ++t) {
+        const int dim = 16 * t + r16;
+        const uint2 v0 = *(const uint2*)(Vts + dim * VLD + 32 * qq + 4 * g4);
+        const uint2 v1 = *(const uint2*)(Vts + dim * VLD + 32 * qq + 16 + 4 * g4);
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t], 0, 0, 0);
+      }
+    }
+  };
+  // blocks in pairs; a block past the range (odd count) sees only masked
+  // keys and leaves m, l and O unchanged
+  for (int kb = kbeg; kb < kend; kb += 2 * AT_KB) {
+    block(kb, std::integral_constant<int, 0>{});
+    block(kb + AT_KB, std::integral_constant<int, 1>{});
   }
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
 
   // O lane layout: row 4 g4 + r of the wave, dim 16 t + r16
   const long base = ((long)split * a.Hkv + g) * nrows;
@@ -176,7 +239,7 @@ __global__ __launch_bounds__(AT_THREADS) void k_tree_attn(AttnArgs a) {
       const int orow = rb * AT_ROWS + wave * 16 + 4 * g4 + r;
       if (orow < nrows) a.opart[(base + orow) * HD + 16 * t + r16] = o[t][r];
     }
-  if (row_ok && g4 == 0) a.mlpart[base + row] = make_float2(mx, l);
+  if (row_ok && g4 == 0) a.mlpart[base + row] = make_float2(m, l);
 }
 
 // out[i][h][:] for row (i, hh) of key/value head g = h / group.
@@ -203,10 +266,15 @@ __global__ void k_tree_attn_combine(AttnArgs a, float* __restrict__ out) {
   out[((long)i * a.Hq + h) * HD + dim] = den > 0.f ? num / den : 0.f;
 }
 
+// Key ranges: about DT_ATTN_WGS workgroups (several per CU, so waves hide each
+// other's latencies) with whole 64-key blocks per range.
+#ifndef DT_ATTN_WGS
+#define DT_ATTN_WGS 512
+#endif
 static void attn_plan(int n, int P, int Hkv, int group, int* nsplit, int* kps) {
   const int keys = P + n;
   const int rblocks = (n * group + AT_ROWS - 1) / AT_ROWS;
-  int s = (512 + Hkv * rblocks - 1) / (Hkv * rblocks);
+  int s = (DT_ATTN_WGS + Hkv * rblocks - 1) / (Hkv * rblocks);
   const int maxs = (keys + AT_KB - 1) / AT_KB;
   if (s > maxs) s = maxs;
   if (s < 1) s = 1;
@@ -260,12 +328,22 @@ extern "C" int tree_attention_verify(const void* q, const void* k_prefix, const 
   a.opart = (float*)workspace;
   a.mlpart = (float2*)((char*)workspace +
                        ((size_t)a.nsplit * rows * HD * 4 + 255) / 256 * 256);
-  hipStream_t st = (hipStream_t)stream;
-  const int rblocks = (n_tree * a.group + AT_ROWS - 1) / AT_ROWS;
-  hipLaunchKernelGGL(k_tree_attn, dim3(Hkv, rblocks, a.nsplit), dim3(AT_THREADS), 0, st, a);
-  if (hipGetLastError() != hipSuccess) return DT_EHIP;
-  const long tot = (long)Hkv * n_tree * a.group * HD;
-  hipLaunchKernelGGL(k_tree_attn_combine, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
-                     a, out);
-  return hipGetLastError() == hipSuccess ? DT_OK : DT_EHIP;
+  struct Ctx {
+    AttnArgs a;
+    float* out;
+    hipStream_t st;
+  } ctx{a, out, (hipStream_t)stream};
+  auto run = [](void* p) -> hipError_t {
+    Ctx& c = *(Ctx*)p;
+    const int rblocks = (c.a.n * c.a.group + AT_ROWS - 1) / AT_ROWS;
+    hipLaunchKernelGGL(k_tree_attn, dim3(c.a.Hkv, rblocks, c.a.nsplit), dim3(AT_THREADS), 0,
+                       c.st, c.a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long tot = (long)c.a.Hkv * c.a.n * c.a.group * HD;
+    hipLaunchKernelGGL(k_tree_attn_combine, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0,
+                       c.st, c.a, c.out);
+    return hipGetLastError();
+  };
+  return dt::timed_launch(DT_K_ATTN, ctx.st, run, &ctx) == hipSuccess ? DT_OK : DT_EHIP;
 }

@@ -174,6 +174,14 @@ hipError_t timed(int cls, hipStream_t st, F&& launch) {
   return e;
 }
 
+}  // namespace
+
+hipError_t dt::timed_launch(int cls, hipStream_t st, hipError_t (*fn)(void*), void* ctx) {
+  return timed(cls, st, [&] { return fn(ctx); });
+}
+
+namespace {
+
 void collect_pending() {
   for (auto& r : g_timing.pending) {
     float ms = 0.f;

@@ -158,6 +158,10 @@ hipError_t launch_beam_step(const BeamArgs& b, hipStream_t st);
 hipError_t launch_fill_rows(int rows, int Mp, const int32_t* tok_in, int32_t* tok,
                             int32_t* src, hipStream_t st);
 
+// Runs fn(ctx) bracketed by timing events of kernel class cls when kernel
+// timing is on (dartree_timing_enable).
+hipError_t timed_launch(int cls, hipStream_t st, hipError_t (*fn)(void*), void* ctx);
+
 hipError_t launch_prune(const float* pool_score, const int32_t* pool_parent,
                         const int32_t* n_valid, int R, int D, int W, int B, float beta,
                         int32_t* sel_node, int32_t* sel_parent, int32_t* sel_depth,

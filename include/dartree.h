@@ -270,7 +270,8 @@ typedef enum {
   DT_K_HEAD = 2,    /* corrected-logit head + per-tile softmax/top-k      */
   DT_K_MERGE = 3,   /* per-row merge and per-request beam select          */
   DT_K_REDUCE = 4,  /* split-K reductions (GELU / residual epilogues)     */
-  DT_K_COUNT = 5
+  DT_K_ATTN = 5,    /* tree-attention verification layer (both kernels)   */
+  DT_K_COUNT = 6
 } dt_kernel_class;
 
 /*
