@@ -275,6 +275,73 @@ def heap_prune(score, parent, n_valid, B: int, beta: float) -> set:
 
 
 # ----------------------------------------------------------------------------
+# sequential heap-interleaved best-first construction (the per-node baseline)
+# ----------------------------------------------------------------------------
+@dataclass
+class SeqTree:
+    """Tree built one head call per expanded node, in pop order."""
+    tok: np.ndarray          # [n] int64
+    parent: np.ndarray       # [n] index of the parent in this list, -1 at depth 1
+    depth: np.ndarray        # [n] 1-based depth
+    score: np.ndarray        # [n] float64 accumulated log-prob
+    n: int
+    head_calls: int
+
+
+def sequential_best_first(head: OracleHead, h: np.ndarray, s0: np.ndarray, root_tok: int,
+                          D: int, k: int, B: int, beta: float, T: float) -> SeqTree:
+    """Best-first tree growth with a max-heap and one head call per expanded
+    node: the costly alternative the pages set against depth-wise batching
+    ("DARTree: Teaching a Chain-Trained Corrector to Think in Trees", Core
+    Mechanism; "Technische Samenvatting: DARTree", Experimentele Resultaten,
+    ablation of sequential heap-interleaved correction against depth-wise
+    batching).
+
+    Reading used here (the pages give the idea, not the steps): the root is
+    expanded first (one head call, h_1); every popped node is appended to the
+    tree and, unless the tree holds B nodes or the node sits at depth D, is
+    expanded at once (one head call on its own row: its parent's updated
+    state, its token and h_{depth+1}) and its top-k children are pushed.  The
+    heap orders by (score + beta * depth desc, depth asc, push order asc).
+    Children, scores and carried states are exactly those of the batched
+    step for the same row.
+    """
+    out_tok, out_par, out_depth, out_score = [], [], [], []
+    heap = []
+    pushed = 0
+    calls = 0
+
+    def expand(state, tok, depth, score, node_index):
+        # one head call on one row; returns the row's updated state
+        nonlocal pushed, calls
+        calls += 1
+        s_new = state_update(head, np.asarray(state, np.float64)[None, :], [int(tok)], h[depth])[0]
+        lp = log_softmax_T(head.logits(s_new[None, :])[0], T)
+        toks, lps = topk_children(lp, k)
+        for r in range(toks.size):
+            sc = score + float(lps[r])
+            d = depth + 1
+            heapq.heappush(heap, (-(sc + beta * d), d, pushed, int(toks[r]), node_index, sc,
+                                  s_new))
+            pushed += 1
+        return s_new
+
+    expand(s0, root_tok, 0, 0.0, -1)
+    while heap and len(out_tok) < B:
+        _, d, _, tok, par, sc, parent_state = heapq.heappop(heap)
+        i = len(out_tok)
+        out_tok.append(tok)
+        out_par.append(par)
+        out_depth.append(d)
+        out_score.append(sc)
+        if len(out_tok) < B and d < D:
+            expand(parent_state, tok, d, sc, i)
+    n = len(out_tok)
+    return SeqTree(np.array(out_tok, np.int64), np.array(out_par, np.int64),
+                   np.array(out_depth, np.int64), np.array(out_score, np.float64), n, calls)
+
+
+# ----------------------------------------------------------------------------
 # ancestor mask
 # ----------------------------------------------------------------------------
 def tree_mask(parent: np.ndarray, n: int, B: int) -> np.ndarray:

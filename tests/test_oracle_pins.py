@@ -284,6 +284,105 @@ def test_survivor_tie_break_on_exact_ties():
     assert tree.score[1, 1] == tree.score[1, 2]
 
 
+
+# ----------------------------------------------------------------------------
+# sequential heap-interleaved best-first construction
+# ----------------------------------------------------------------------------
+def _full_topk_tree(head, h, s0, root, D, k, T):
+    """Brute force: every node of the k-ary tree to depth D, where a node's
+    children are the k best tokens of its row (logp desc, token asc) by
+    scipy's log_softmax; returns {token path: score}."""
+    out = {}
+
+    def rec(state, tok, depth, path, score):
+        if depth == D:
+            return
+        s = O.state_update(head, np.asarray(state)[None], [tok], h[depth])
+        z = head.logits(s)[0]
+        lp = scipy.special.log_softmax(z / T)
+        order = np.lexsort((np.arange(lp.size), -lp))[:k]
+        for c in order:
+            p = path + (int(c),)
+            out[p] = score + float(lp[c])
+            rec(s[0], int(c), depth + 1, p, out[p])
+
+    rec(np.asarray(s0, np.float64), root, 0, (), 0.0)
+    return out
+
+
+def _seq_paths(tree):
+    paths = []
+    for i in range(tree.n):
+        p, j = [], i
+        while j >= 0:
+            p.append(int(tree.tok[j]))
+            j = int(tree.parent[j])
+        paths.append(tuple(reversed(p)))
+    return paths
+
+
+@settings(max_examples=12, deadline=None)
+@given(B=st.integers(1, 30), beta=st.floats(-1.5, 0.0), seed=st.integers(0, 50),
+       T=st.sampled_from([0.5, 1.0, 2.0]))
+def test_sequential_best_first_is_top_b_of_the_full_tree(B, beta, seed, T):
+    # Lemma 1 on the whole k-ary tree: with beta <= 0 the sequential pops are
+    # the B best nodes of the full tree by score + beta * depth
+    D, k = 3, 3
+    head = tiny_head(V=9, d=6, seed=seed)
+    h, s0 = _inputs(head, D, seed=seed + 100)
+    full = _full_topk_tree(head, h, s0, 1, D, k, T)
+    seq = O.sequential_best_first(head, h, s0, 1, D=D, k=k, B=B, beta=beta, T=T)
+    ranked = sorted(full, key=lambda p: -(full[p] + beta * len(p)))
+    want = set(ranked[:min(B, len(full))])
+    paths = _seq_paths(seq)
+    assert seq.n == min(B, len(full))
+    assert set(paths) == want
+    for i, p in enumerate(paths):
+        assert abs(seq.score[i] - full[p]) < 1e-12
+        assert seq.depth[i] == len(p)
+        # ancestor-closed, parents popped first
+        assert seq.parent[i] < i and (seq.parent[i] == -1) == (len(p) == 1)
+    # pop order is best-first: priorities never increase
+    prio = seq.score + beta * seq.depth
+    assert np.all(np.diff(prio) <= 1e-12)
+
+
+def test_sequential_matches_batched_prune_when_beam_keeps_everything():
+    D, k, B = 3, 3, 11
+    head = tiny_head(V=12, d=6, seed=7)
+    h, s0 = _inputs(head, D, seed=3)
+    for beta in (0.0, -0.3):
+        tree = O.build_supertree(head, h, s0, 2, D=D, W=k ** D, k=k, T=1.0)
+        vt = O.prune_topB(tree.score, tree.parent, tree.n_valid, B, beta)
+        want = set()
+        for node in vt.node:
+            t, j = divmod(int(node), k ** D)
+            p = []
+            while t >= 0:
+                p.append(int(tree.tok[t, j]))
+                j = int(tree.parent[t, j]); t -= 1
+            want.add(tuple(reversed(p)))
+        seq = O.sequential_best_first(head, h, s0, 2, D=D, k=k, B=B, beta=beta, T=1.0)
+        assert set(_seq_paths(seq)) == want
+        # one head call per expanded node: the root plus every popped node that
+        # is neither the last one nor at depth D
+        expanded = sum(1 for i in range(seq.n - 1) if seq.depth[i] < D)
+        assert seq.head_calls == 1 + expanded
+
+
+def test_sequential_T0_is_the_greedy_chain():
+    head = tiny_head(V=40, d=8)
+    h, s0 = _inputs(head, 6)
+    toks, _ = _greedy_chain(head, h, s0, 3, 6)
+    for B in (3, 6, 10):
+        seq = O.sequential_best_first(head, h, s0, 3, D=6, k=4, B=B, beta=0.0, T=0.0)
+        n = min(B, 6)
+        assert seq.n == n and seq.head_calls == n
+        assert seq.tok.tolist() == toks[:n]
+        assert seq.parent.tolist() == list(range(-1, n - 1))
+        assert np.all(seq.score == 0.0)
+
+
 # ----------------------------------------------------------------------------
 # deferred pruning (Lemma 1), ancestor closure, mask
 # ----------------------------------------------------------------------------
