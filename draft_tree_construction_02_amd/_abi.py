@@ -26,6 +26,7 @@ EXPORTS = [
     "dartree_status_string", "dartree_version", "pack_head_bytes", "pack_head",
     "build_supertree_workspace_size", "build_supertree",
     "head_step_workspace_size", "state_update", "corrected_topk",
+    "build_tree_sequential_workspace_size", "build_tree_sequential",
     "prune_topB", "build_tree_mask",
     "tree_attention_workspace_size", "tree_attention_verify",
     "dartree_timing_enable", "dartree_timing_reset", "dartree_timing_read",
@@ -66,6 +67,9 @@ def lib():
             "build_supertree": (i32, [hp, vp, vp, vp, i32, i32, i32, i32, f32,
                                       vp, vp, vp, vp, vp, sz, vp]),
             "head_step_workspace_size": (sz, [hp, i32, i32]),
+            "build_tree_sequential_workspace_size": (sz, [hp, i32, i32, i32]),
+            "build_tree_sequential": (i32, [hp, vp, vp, vp, i32, i32, i32, f32, f32,
+                                            vp, vp, vp, vp, vp, vp, sz, vp]),
             "state_update": (i32, [hp, vp, vp, vp, i32, vp, vp, sz, vp]),
             "corrected_topk": (i32, [hp, vp, i32, i32, f32, vp, vp, vp, vp, sz, vp]),
             "prune_topB": (i32, [vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]),
@@ -190,6 +194,38 @@ def build_supertree(head: Head, h, s0, root_tok, D: int, W: int, k: int, T: floa
                                _ptr(out["pool_score"]), _ptr(out["n_valid"]), _ptr(ws),
                                ws.numel(), _stream(stream))
     _check(rc, "build_supertree")
+    return out
+
+
+def build_tree_sequential_workspace_size(head: Head, D, k, B) -> int:
+    return int(lib().build_tree_sequential_workspace_size(head.ref, D, k, B))
+
+
+def build_tree_sequential(head: Head, h, s0, root_tok, D: int, k: int, B: int, beta: float,
+                          T: float, workspace=None, out=None, stream=None) -> dict:
+    """Sequential best-first construction of one request, one head call per
+    expanded node.
+
+    h [D][d] f32, s0 [d] f32, root_tok [1] int32 -> dict of tok, parent, depth,
+    score ([B], pop order) and n ([1])."""
+    _dev(h, torch.float32, "h", (D, head.d))
+    _dev(s0, torch.float32, "s0", (head.d,))
+    _dev(root_tok, torch.int32, "root_tok", (1,))
+    dev = head.device
+    if out is None:
+        out = dict(tok=torch.empty((B,), dtype=torch.int32, device=dev),
+                   parent=torch.empty((B,), dtype=torch.int32, device=dev),
+                   depth=torch.empty((B,), dtype=torch.int32, device=dev),
+                   score=torch.empty((B,), dtype=torch.float32, device=dev),
+                   n=torch.empty((1,), dtype=torch.int32, device=dev))
+    need = build_tree_sequential_workspace_size(head, D, k, B)
+    ws = _workspace(need, dev, workspace)
+    rc = lib().build_tree_sequential(head.ref, _ptr(h), _ptr(s0), _ptr(root_tok), D, k, B,
+                                     float(beta), float(T), _ptr(out["tok"]),
+                                     _ptr(out["parent"]), _ptr(out["depth"]),
+                                     _ptr(out["score"]), _ptr(out["n"]), _ptr(ws), ws.numel(),
+                                     _stream(stream))
+    _check(rc, "build_tree_sequential")
     return out
 
 

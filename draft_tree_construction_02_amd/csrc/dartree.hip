@@ -206,6 +206,9 @@ struct DepthIo {
   int rows;
   float* s_out;             // updated states, rows_out rows of d
   int rows_out;
+  const int32_t* skip = nullptr;   // device flag: launches do nothing when set
+  bool prep = true;                // bf16: build the x planes here (else already built)
+  const float* x_dense = nullptr;  // fp32: dense x rows instead of the gather
 };
 
 // s' = s_parent + GELU(x W1) W2 with x = E[tok] + h_t: (bf16 heads) x is
@@ -215,7 +218,7 @@ hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hip
   const int bf = hd->wdtype == DT_BF16, d = hd->d;
   const int packed = hd->layout == DT_LAYOUT_PACKED;
   hipError_t e = hipSuccess;
-  if (bf) {
+  if (bf && io.prep) {
     PrepArgs pr;
     pr.E = (const uint16_t*)hd->E;
     pr.d = d;
@@ -231,8 +234,11 @@ hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hip
     if (e != hipSuccess) return e;
   }
   GemmArgs g1;
+  g1.skip = io.skip;
   g1.pa = PackedA{w.x_hi, w.x_lo, d};
-  g1.a.gather = 1;
+  g1.a.gather = io.x_dense ? 0 : 1;
+  g1.a.a = io.x_dense;
+  g1.a.lda = d;
   g1.a.E = hd->E;
   g1.a.ldE = d;
   g1.a.tok = io.tok;
@@ -251,6 +257,7 @@ hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hip
   e = timed(DT_K_GEMM1, st, [&] { return launch_gemm(g1, st); });
   if (e != hipSuccess) return e;
   ReduceArgs r1;
+  r1.skip = io.skip;
   r1.part = w.part;
   r1.splits = w.splits1;
   r1.Mp = w.Mp;
@@ -265,6 +272,7 @@ hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hip
   if (e != hipSuccess) return e;
 
   GemmArgs g2;
+  g2.skip = io.skip;
   g2.pa = PackedA{w.H_hi, w.H_lo, 4 * d};
   g2.a.a = w.H;
   g2.a.lda = 4 * d;
@@ -280,6 +288,7 @@ hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hip
   e = timed(DT_K_GEMM2, st, [&] { return launch_gemm(g2, st); });
   if (e != hipSuccess) return e;
   ReduceArgs r2;
+  r2.skip = io.skip;
   r2.part = w.part;
   r2.splits = w.splits2;
   r2.Mp = w.Mp;
@@ -310,9 +319,10 @@ int head_tiles_for(const dt_head* hd, int Mp) {
 
 hipError_t run_head(const dt_head* hd, const StepWs& w, const float* s, int rows, int k, float T,
                     int32_t* cand_tok, float* cand_lp, float* lse, hipStream_t st,
-                    bool final_merge = true) {
+                    bool final_merge = true, const int32_t* skip = nullptr) {
   const bool greedy = T == 0.f;
   HeadArgs p;
+  p.skip = skip;
   p.pa = PackedA{w.s_hi, w.s_lo, hd->d};
   p.a.a = s;
   p.a.lda = hd->d;
@@ -334,7 +344,7 @@ hipError_t run_head(const dt_head* hd, const StepWs& w, const float* s, int rows
   if (!final_merge)
     return timed(DT_K_MERGE, st, [&] {
       return launch_merge_part(w.ms_part, w.key_part, rows, head_tiles(p), p.k, p.kmax, w.ms2,
-                               w.key2, st);
+                               w.key2, st, skip);
     });
   return timed(DT_K_MERGE, st, [&] {
     return launch_merge(w.ms_part, w.key_part, rows, head_tiles(p), p.k, k, p.kmax, greedy,
@@ -526,6 +536,100 @@ int pack_head(const dt_head* src, void* dst, size_t dst_bytes, dt_head* packed, 
   packed->W2t = w2;
   packed->Ut = u;
   return DT_OK;
+}
+
+// ---------------------------------------------------------------- sequential
+struct SeqWs {
+  StepWs step;
+  SeqArgs a;
+};
+
+static SeqWs carve_seq(Carver& c, const dt_head* h, int D, int k, int B, bool greedy) {
+  SeqWs s{};
+  s.step = carve_step(c, h, 1, k);
+  const int d = h->d, keff = greedy ? 1 : k, cap = B * keff;
+  SeqArgs& a = s.a;
+  a.state = c.take<float>((size_t)(B + 1) * d);
+  if (h->wdtype != DT_BF16) a.x_f32 = c.take<float>((size_t)s.step.Mp * d);
+  a.c_tok = c.take<int32_t>(cap);
+  a.c_par = c.take<int32_t>(cap);
+  a.c_depth = c.take<int32_t>(cap);
+  a.c_row = c.take<int32_t>(cap);
+  a.c_score = c.take<float>(cap);
+  a.c_alive = c.take<uint32_t>((cap + 31) / 32);
+  a.ctl = c.take<int32_t>(SEQ_CTL_WORDS);
+  a.cur_score = c.take<float>(1);
+  return s;
+}
+
+static int seq_args_ok(const dt_head* head, int D, int k, int B) {
+  if (!head_ok(head)) return DT_EINVAL;
+  if (D < 1 || k < 1 || k > head->V || B < 1) return DT_EINVAL;
+  if (D > DT_MAX_DEPTH || k > DT_MAX_K || B > DT_MAX_B) return DT_EUNSUPPORTED;
+  return DT_OK;
+}
+
+size_t build_tree_sequential_workspace_size(const dt_head* head, int D, int k, int B) {
+  if (seq_args_ok(head, D, k, B) != DT_OK) return 0;
+  Carver c(nullptr);
+  carve_seq(c, head, D, k, B, false);
+  return c.off;
+}
+
+int build_tree_sequential(const dt_head* head, const float* h, const float* s0,
+                          const int32_t* root_tok, int D, int k, int B, float beta, float T,
+                          int32_t* tok, int32_t* parent, int32_t* depth, float* score,
+                          int32_t* n_out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  int rc = seq_args_ok(head, D, k, B);
+  if (rc != DT_OK) return rc;
+  if (!h || !s0 || !root_tok || !tok || !parent || !depth || !score || !n_out) return DT_EINVAL;
+  if (!(T >= 0.f) || !isfinite(T) || !(beta <= 0.f) || !isfinite(beta)) return DT_EINVAL;
+  const size_t need = build_tree_sequential_workspace_size(head, D, k, B);
+  if (!workspace || workspace_bytes < need) return DT_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const bool greedy = T == 0.f, bf = head->wdtype == DT_BF16;
+  Carver c(workspace);
+  SeqWs sw = carve_seq(c, head, D, k, B, greedy);
+  const StepWs& w = sw.step;
+  SeqArgs& a = sw.a;
+  const int d = head->d;
+  a.D = D; a.k = k; a.B = B; a.kmax = kmax_for(k, greedy);
+  a.S = merge_splits(head_tiles_for(head, w.Mp));
+  a.greedy = greedy; a.Mp = w.Mp; a.d = d; a.beta = beta;
+  a.ms2 = w.ms2; a.key2 = w.key2;
+  a.out_tok = tok; a.out_par = parent; a.out_depth = depth; a.out_score = score;
+  a.n_out = n_out;
+  a.E = head->E; a.h = h;
+  if (bf) {
+    a.x_hi = w.x_hi;
+    a.x_lo = w.x_lo;
+  }
+  hipError_t e = launch_seq_init(a, s0, root_tok, st);
+  // B call slots: the root's call and one per popped node that is expanded;
+  // slots past the last expansion do nothing (device flag)
+  for (int slot = 0; slot < B && e == hipSuccess; ++slot) {
+    DepthIo io;
+    io.s_prev = a.state;
+    io.tok = nullptr;
+    io.src = a.ctl + SEQ_CUR_ROW;
+    io.h = h;
+    io.h_req_stride = 0;
+    io.rpr = 1;
+    io.rows = 1;
+    io.s_out = a.state + (long)slot * d;
+    io.rows_out = 1;
+    io.skip = a.ctl + SEQ_SKIP;
+    io.prep = false;
+    io.x_dense = bf ? nullptr : a.x_f32;
+    e = run_update(head, w, io, st);
+    if (e != hipSuccess) break;
+    e = run_head(head, w, io.s_out, 1, k, T, w.cand_tok, w.cand_lp, w.lse, st, false,
+                 io.skip);
+    if (e != hipSuccess) break;
+    e = timed(DT_K_MERGE, st, [&] { return launch_seq_step(a, slot, st); });
+  }
+  return e == hipSuccess ? DT_OK : DT_EHIP;
 }
 
 int prune_topB(const float* pool_score, const int32_t* pool_parent, const int32_t* n_valid, int R,

@@ -420,6 +420,7 @@ __device__ __forceinline__ float* tile_f32(const ASrc& src, const float* __restr
 // ----------------------------------------------------------------------------
 template <int MT, int NBUF, bool PW>
 __global__ __launch_bounds__(64 * DT_WV_GEMM) void k_gemm_bf16(GemmArgs g) {
+  if (g.skip && *g.skip) return;
   constexpr int NW = DT_NW_GEMM, WV = DT_WV_GEMM;
   using Cfg = BfCfg<MT, NBUF, NW, WV>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg::LDS];
@@ -448,6 +449,7 @@ __global__ __launch_bounds__(64 * DT_WV_GEMM) void k_gemm_bf16(GemmArgs g) {
 
 template <int MT, bool GATHER>
 __global__ __launch_bounds__(NT) void k_gemm_f32(GemmArgs g) {
+  if (g.skip && *g.skip) return;
   __shared__ __attribute__((aligned(16))) unsigned char smem[F32Cfg<MT>::LDS];
   constexpr int Mp = 16 * MT;
   const int tile = blockIdx.x, split = blockIdx.y;
@@ -471,6 +473,7 @@ __global__ __launch_bounds__(NT) void k_gemm_f32(GemmArgs g) {
 // Rows >= rows are zero.
 template <int G>
 __global__ __launch_bounds__(128) void k_reduce(ReduceArgs r) {
+  if (r.skip && *r.skip) return;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const int n8 = r.N / 8;
   const long grp = gid / G;
@@ -570,6 +573,7 @@ __device__ __forceinline__ void head_epilogue(const HeadArgs& p, const float* Cs
 template <int MT, int NBUF, int KMAX, bool PW>
 __global__ __launch_bounds__(64 * DT_WV_HEAD)
 __attribute__((amdgpu_waves_per_eu(DT_HEAD_WPE, 8))) void k_head_bf16(HeadArgs p) {
+  if (p.skip && *p.skip) return;
   constexpr int NW = DT_NW_HEAD;
   constexpr int TN = TN_HEAD;
   __shared__ __attribute__((aligned(16))) unsigned char smem[BfCfg<MT, NBUF, NW, DT_WV_HEAD>::LDS];
@@ -598,6 +602,7 @@ __attribute__((amdgpu_waves_per_eu(DT_HEAD_WPE, 8))) void k_head_bf16(HeadArgs p
 
 template <int MT, int KMAX>
 __global__ __launch_bounds__(NT) void k_head_f32(HeadArgs p) {
+  if (p.skip && *p.skip) return;
   __shared__ __attribute__((aligned(16))) unsigned char smem[F32Cfg<MT>::LDS];
   const int tile = blockIdx.x;
   const float* Cs = tile_f32<MT, false>(p.a, (const float*)p.Ut, p.d, p.V, tile * TN_F, 0, p.d,

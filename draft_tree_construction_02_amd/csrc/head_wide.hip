@@ -85,6 +85,7 @@ __device__ __forceinline__ void hw_load_b(u32x4 (&b)[HW_NW], const uint16_t* wp)
 template <int MT, int KMAX>
 __global__ __launch_bounds__(64 * HW_WAVES)
 __attribute__((amdgpu_waves_per_eu(2))) void k_head_wide(HeadArgs p) {
+  if (p.skip && *p.skip) return;
   using C = HwCfg<MT, KMAX>;
   constexpr int Mp = C::Mp;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];

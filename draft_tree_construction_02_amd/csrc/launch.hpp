@@ -42,7 +42,10 @@ struct PackedA {
 enum Epi { EPI_GELU = 0, EPI_RESID = 1 };
 
 // Split-K partial products part[split][Mp][N] of Y = A Wt^T, Wt [N][K].
+// skip (optional, device): when *skip != 0 the launch does nothing; used by
+// the sequential construction, whose number of head calls is data-dependent.
 struct GemmArgs {
+  const int32_t* skip = nullptr;
   PackedA pa;                 // bf16 path, packed activation planes
   ASrc a;                     // fp32 path
   const void* Wt = nullptr;
@@ -60,6 +63,7 @@ struct GemmArgs {
 // Writes out [rows_out][N] fp32 (if out) and the packed hi/lo planes
 // [Mp][N] (if out_hi); rows >= rows are zero.
 struct ReduceArgs {
+  const int32_t* skip = nullptr;
   const float* part = nullptr;
   int splits = 1, Mp = 0, N = 0, rows = 0, rows_out = 0;
   int epi = EPI_GELU;
@@ -78,6 +82,7 @@ hipError_t launch_reduce(const ReduceArgs& r, hipStream_t st);
 // Corrected-logit head: per (row, vocabulary tile) the tile's max, sum of
 // exp(y - max) and top-kmax keys of y = z * inv_T (z raw when greedy).
 struct HeadArgs {
+  const int32_t* skip = nullptr;
   PackedA pa;                 // bf16 path: s' hi/lo
   ASrc a;                     // fp32 path: dense s'
   const void* Ut = nullptr;
@@ -113,7 +118,7 @@ hipError_t launch_merge(const float2* ms_part, const uint64_t* key_part, int row
 // First pass only (the beam step folds the range results itself).
 hipError_t launch_merge_part(const float2* ms_part, const uint64_t* key_part, int rows,
                              int ntiles, int kt, int kmax, float2* ms2, uint64_t* key2,
-                             hipStream_t st);
+                             hipStream_t st, const int32_t* skip = nullptr);
 
 // x = E[tok[m]] + h[(m / rpr) * h_req_stride] written as packed hi/lo planes
 // [Mp][d] (bf16 heads); rows m >= rows or with tok[m] < 0 are zero.
@@ -157,6 +162,50 @@ hipError_t launch_beam_init(int R, int W, int Mp, const int32_t* root_tok, int32
 hipError_t launch_beam_step(const BeamArgs& b, hipStream_t st);
 hipError_t launch_fill_rows(int rows, int Mp, const int32_t* tok_in, int32_t* tok,
                             int32_t* src, hipStream_t st);
+
+// Sequential best-first construction (sequential.hip).  ctl holds the
+// control words below; candidates are pushed in order, each expansion adding
+// its top-keff children.
+enum SeqCtl {
+  SEQ_N_OUT = 0,      // nodes in the output tree
+  SEQ_N_CAND = 1,     // candidates pushed so far
+  SEQ_SKIP = 2,       // 1: the remaining call slots do nothing
+  SEQ_CUR_OUT = 3,    // output index of the node being expanded (-1: root)
+  SEQ_CUR_DEPTH = 4,  // its depth (0: root)
+  SEQ_CUR_ROW = 5,    // state row of its parent's update (the residual source)
+  SEQ_CUR_TOK = 6,    // its token
+  SEQ_CALLS = 7,      // head calls made
+  SEQ_CTL_WORDS = 8
+};
+constexpr int SEQ_MAX_CAND = 16384;   // DT_MAX_B * DT_MAX_K
+struct SeqArgs {
+  int D = 0, k = 0, B = 0, kmax = 1, S = 1, greedy = 0, Mp = 0, d = 0;
+  float beta = 0.f;
+  const float2* ms2 = nullptr;         // merge range results of row 0 [S]
+  const uint64_t* key2 = nullptr;      // [S][kmax]
+  int32_t* ctl = nullptr;              // [SEQ_CTL_WORDS]
+  float* cur_score = nullptr;          // [1] score of the node being expanded
+  int32_t* c_tok = nullptr;            // candidates [B * keff]
+  int32_t* c_par = nullptr;
+  int32_t* c_depth = nullptr;
+  int32_t* c_row = nullptr;
+  float* c_score = nullptr;
+  uint32_t* c_alive = nullptr;         // bitmap
+  float* state = nullptr;              // [B + 1][d] updated states; row B = s0
+  int32_t* out_tok = nullptr;          // [B]
+  int32_t* out_par = nullptr;
+  int32_t* out_depth = nullptr;
+  float* out_score = nullptr;
+  int32_t* n_out = nullptr;
+  const void* E = nullptr;             // embedding (bf16 or fp32, as the head)
+  const float* h = nullptr;            // [D][d]
+  uint16_t* x_hi = nullptr;            // bf16 heads: packed x planes [Mp][d]
+  uint16_t* x_lo = nullptr;
+  float* x_f32 = nullptr;              // fp32 heads: dense x [Mp][d]
+};
+hipError_t launch_seq_init(const SeqArgs& a, const float* s0, const int32_t* root_tok,
+                           hipStream_t st);
+hipError_t launch_seq_step(const SeqArgs& a, int slot, hipStream_t st);
 
 // Runs fn(ctx) bracketed by timing events of kernel class cls when kernel
 // timing is on (dartree_timing_enable).

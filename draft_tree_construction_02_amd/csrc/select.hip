@@ -27,7 +27,9 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_merge_part(const float2* __re
                                                               const uint64_t* __restrict__ key_part,
                                                               int ntiles, int kt,
                                                               float2* __restrict__ ms2,
-                                                              uint64_t* __restrict__ key2) {
+                                                              uint64_t* __restrict__ key2,
+                                                              const int32_t* skip) {
+  if (skip && *skip) return;
   constexpr int BATCH = 4;
   const int row = blockIdx.x, s = blockIdx.y, S = gridDim.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -151,11 +153,11 @@ __global__ __launch_bounds__(64) void k_merge_final(const float2* __restrict__ m
 
 hipError_t launch_merge_part(const float2* ms_part, const uint64_t* key_part, int rows,
                              int ntiles, int kt, int kmax, float2* ms2, uint64_t* key2,
-                             hipStream_t st) {
+                             hipStream_t st, const int32_t* skip) {
   const int S = merge_splits(ntiles);
 #define DT_MERGE1(KM)                                                                        \
   hipLaunchKernelGGL(k_merge_part<KM>, dim3(rows, S), dim3(MERGE_THREADS), 0, st, ms_part,     \
-                     key_part, ntiles, kt, ms2, key2)
+                     key_part, ntiles, kt, ms2, key2, skip)
   switch (kmax) {
     case 1: DT_MERGE1(1); break;
     case 4: DT_MERGE1(4); break;
@@ -178,7 +180,7 @@ hipError_t launch_merge(const float2* ms_part, const uint64_t* key_part, int row
   const int S = merge_splits(ntiles);
 #define DT_MERGE(KM)                                                                          \
   hipLaunchKernelGGL(k_merge_part<KM>, dim3(rows, S), dim3(MERGE_THREADS), 0, st, ms_part,      \
-                     key_part, ntiles, kt, ms2, key2);                                          \
+                     key_part, ntiles, kt, ms2, key2, nullptr);                                 \
   hipLaunchKernelGGL(k_merge_final<KM>, dim3(rows), dim3(64), 0, st, ms2, key2, S, k, greedy,   \
                      cand_tok, cand_lp, lse)
   switch (kmax) {

@@ -198,6 +198,42 @@ int corrected_topk(const dt_head* head, const float* s, int rows, int k, float T
                    size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Sequential best-first construction (the per-node baseline)               */
+/* ------------------------------------------------------------------------ */
+
+/* Device bytes of workspace build_tree_sequential needs (0 if invalid). */
+size_t build_tree_sequential_workspace_size(const dt_head* head, int D, int k, int B);
+
+/*
+ * build_tree_sequential - the costly alternative to depth-wise batching that
+ * the pages measure against ([P1] Core Mechanism; [P2] Experimentele
+ * Resultaten, ablation of sequential heap-interleaved correction): best-first
+ * growth with a max-heap and ONE HEAD CALL PER EXPANDED NODE, for one
+ * request.  The root is expanded first (h row 0); then the best candidate by
+ * (score + beta * depth desc, depth asc, push order asc) is popped and
+ * appended to the tree, and, unless the tree holds B nodes or the node is at
+ * depth D, expanded at once: the head's state step on its parent's updated
+ * state with its token and h row `depth`, its top-k children (temperature T,
+ * T == 0 the argmax) pushed with score = node score + logp.  Repeats until B
+ * nodes or no candidate is left.  Head calls = 1 + expanded popped nodes.
+ *   h [D][d] f32, s0 [d] f32, root_tok [1] i32 (device)
+ * Outputs, in pop order (entries >= *n_out are -1 / -inf):
+ *   tok    [B] i32   node token
+ *   parent [B] i32   index of the parent entry (earlier), -1 at depth 1
+ *   depth  [B] i32   1..D
+ *   score  [B] f32   accumulated log-probability (0 when T == 0)
+ *   n_out  [1] i32   nodes in the tree
+ * 1 <= k <= min(V, DT_MAX_K), 1 <= B <= DT_MAX_B, 1 <= D <= DT_MAX_DEPTH,
+ * beta <= 0 finite, T >= 0 finite.  Everything runs on `stream`: B call
+ * slots are enqueued and the ones after the last expansion do nothing.
+ */
+int build_tree_sequential(const dt_head* head, const float* h, const float* s0,
+                          const int32_t* root_tok, int D, int k, int B, float beta, float T,
+                          int32_t* tok, int32_t* parent, int32_t* depth, float* score,
+                          int32_t* n_out, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Deferred best-first pruning and the verification mask                    */
 /* ------------------------------------------------------------------------ */
 

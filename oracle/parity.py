@@ -223,3 +223,73 @@ def compare_exact(ora: O.Supertree, dev, tol) -> list:
         if not err <= tol:
             out.append(f"scores differ from the oracle build by {err:.3g}")
     return out
+
+
+def check_sequential(head, h, s0, root_tok, D, k, B, beta, T, dev, tol, tau) -> Report:
+    """Teacher-forced check of a device-built sequential best-first tree.
+
+    dev: dict of tok, parent, depth, score ([B], pop order) and n.  The
+    oracle replays the heap along the device's pops: each popped node must be
+    a candidate (a top-k child of its parent in fp64, or within tau of the
+    k-th child), its fp64 priority must be within tau of the best candidate
+    left, its score within tol of the fp64 path score, and every expansion
+    the device performs is repeated in fp64 from the device's token path.
+    """
+    rep = Report()
+    n = int(np.asarray(dev["n"]).reshape(-1)[0])
+    tok = np.asarray(dev["tok"]); par = np.asarray(dev["parent"])
+    dep = np.asarray(dev["depth"]); sco = np.asarray(dev["score"], np.float64)
+    cand = {}          # (parent index, token) -> (score, depth)
+    row_lp = {}        # parent index -> (full logp row, top-k tokens, its state)
+    states = {}
+
+    def expand(idx, state, t, depth, score):
+        s_new = O.state_update(head, np.asarray(state, np.float64)[None, :], [int(t)],
+                               h[depth])[0]
+        lp = O.log_softmax_T(head.logits(s_new[None, :])[0], T)
+        toks, lps = O.topk_children(lp, k)
+        row_lp[idx] = (lp, set(int(x) for x in toks), float(lps[-1]) if lps.size else -math.inf,
+                       score)
+        states[idx] = s_new
+        for c, l in zip(toks.tolist(), lps.tolist()):
+            cand[(idx, int(c))] = (score + l, depth + 1)
+
+    expand(-1, s0, root_tok, 0, 0.0)
+    for i in range(n):
+        key = (int(par[i]), int(tok[i]))
+        if key[0] not in row_lp:
+            rep.fail(f"pop {i}: parent {key[0]} was never expanded")
+            return rep
+        if key not in cand:
+            lp, top, kth, psc = row_lp[key[0]]
+            c = key[1]
+            gap = kth - float(lp[c]) if 0 <= c < lp.size else math.inf
+            if T > 0.0 and gap <= tau:
+                rep.exemptions += 1
+                cand[key] = (psc + float(lp[c]), int(dep[i]))
+            else:
+                rep.fail(f"pop {i}: token {c} is not a child of entry {key[0]} (gap {gap:.3g})")
+                return rep
+        sc, d = cand[key]
+        if d != int(dep[i]):
+            rep.fail(f"pop {i}: depth {dep[i]} != {d}")
+        err = abs(float(sco[i]) - sc)
+        rep.max_score_err = max(rep.max_score_err, err)
+        if not err <= tol:
+            rep.fail(f"pop {i}: score {sco[i]:.7g} vs oracle {sc:.7g}")
+        prio = sc + beta * d
+        best = max(v[0] + beta * v[1] for v in cand.values())
+        if best - prio > tau:
+            rep.fail(f"pop {i}: priority {prio:.6g} below the best candidate {best:.6g}")
+        elif best - prio > 0.0:
+            rep.exemptions += 1
+        del cand[key]
+        if i + 1 < B and d < D:
+            # the node carries its parent's updated state (the root's for depth 1)
+            expand(i, states[key[0]], key[1], d, sc)
+    if n < B and cand:
+        rep.fail(f"device stopped after {n} pops with {len(cand)} candidates left")
+    if n > B:
+        rep.fail(f"n = {n} > B")
+    rep.notes.append(dict(head_calls=len(row_lp)))
+    return rep

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     L = A.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -77,6 +77,35 @@ def test_build_supertree_validation():
     bad.Ut = None
     assert build(bad) == DT_EINVAL
     assert build(fake_head(V=4), k=8) == DT_EINVAL        # k > V
+
+
+def seq(hd, D=16, k=8, B=64, beta=0.0, T=1.0, ws=1 << 40, wsp=1, **kw):
+    p = dict(hid=1, s0=1, root=1, tok=1, par=1, depth=1, score=1, n=1)
+    p.update(kw)
+    return A.lib().build_tree_sequential(C.byref(hd), p["hid"], p["s0"], p["root"], D, k, B,
+                                         beta, T, p["tok"], p["par"], p["depth"], p["score"],
+                                         p["n"], wsp, ws, None)
+
+
+def test_build_tree_sequential_validation():
+    h = fake_head()
+    L = A.lib()
+    assert L.build_tree_sequential_workspace_size(C.byref(h), 16, 8, 64) > 0
+    assert L.build_tree_sequential_workspace_size(C.byref(h), 16, 0, 64) == 0
+    assert seq(h, k=0) == DT_EINVAL
+    assert seq(h, B=0) == DT_EINVAL
+    assert seq(h, D=0) == DT_EINVAL
+    assert seq(h, beta=0.5) == DT_EINVAL
+    assert seq(h, beta=float("nan")) == DT_EINVAL
+    assert seq(h, T=-1.0) == DT_EINVAL
+    assert seq(h, k=17) == DT_EUNSUPPORTED
+    assert seq(h, B=1025) == DT_EUNSUPPORTED
+    assert seq(h, D=65) == DT_EUNSUPPORTED
+    assert seq(h, hid=None) == DT_EINVAL
+    assert seq(h, n=None) == DT_EINVAL
+    assert seq(h, ws=10) == DT_EWORKSPACE
+    assert seq(h, wsp=None) == DT_EWORKSPACE
+    assert seq(fake_head(V=4), k=8) == DT_EINVAL
 
 
 def test_pack_head_validation():

@@ -370,6 +370,26 @@ def test_sequential_matches_batched_prune_when_beam_keeps_everything():
         assert seq.head_calls == 1 + expanded
 
 
+def test_sequential_checker_accepts_the_oracle_and_rejects_planted_mistakes():
+    from oracle import parity as P
+    head = tiny_head(V=50, d=8, seed=2)
+    h, s0 = _inputs(head, 5, seed=8)
+    t = O.sequential_best_first(head, h, s0, 3, D=5, k=4, B=20, beta=-0.1, T=1.0)
+    dev = dict(tok=t.tok, parent=t.parent, depth=t.depth, score=t.score, n=[t.n])
+    assert P.check_sequential(head, h, s0, 3, 5, 4, 20, -0.1, 1.0, dev, 1e-9, 1e-9).ok
+    for mut in ("tok", "score", "order"):
+        bad = {k: np.array(v).copy() for k, v in dev.items()}
+        if mut == "tok":
+            bad["tok"][2] = (bad["tok"][2] + 1) % 50
+        elif mut == "score":
+            bad["score"][3] += 1e-6
+        else:
+            for key in ("tok", "parent", "depth", "score"):
+                bad[key][[1, 2]] = bad[key][[2, 1]]
+        assert not P.check_sequential(head, h, s0, 3, 5, 4, 20, -0.1, 1.0, bad, 1e-9,
+                                      1e-9).ok, mut
+
+
 def test_sequential_T0_is_the_greedy_chain():
     head = tiny_head(V=40, d=8)
     h, s0 = _inputs(head, 6)
