@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_4b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sequential", action="store_true",
+                    help="skip the sequential best-first (one head call per node) comparison")
     ap.add_argument("--cpu-builds", type=int, default=1,
                     help="oracle builds timed for cpu_baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -245,9 +247,48 @@ def main():
         "step_weight_stream_gbs": round(bytes_per_step / (ms_per_step * 1e-3) / 1e9, 1),
     }
 
+    if wl.R == 1 and not args.no_sequential:
+        res["sequential_baseline"] = sequential_baseline(A, head, h, s0, root, wl, b_ms, b_wall,
+                                                         bpm_ms, bpm_wall, args.steps)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, hw, req, args.cpu_builds)
     print(json.dumps(res), flush=True)
+
+
+def sequential_baseline(A, head, h, s0, root, wl, b_ms, b_wall, bpm_ms, bpm_wall, steps):
+    """The per-node construction the pages set against depth-wise batching:
+    best-first with one head call per expanded node (same head, same B), timed
+    over a few trees, next to the batched build + prune + mask of the same
+    request."""
+    import torch
+    D, k, B = wl.D, wl.k, wl.B
+    ws = torch.empty(A.build_tree_sequential_workspace_size(head, D, k, B), dtype=torch.uint8,
+                     device="cuda:0")
+    out = None
+    h0, s00, r0 = h[0].contiguous(), s0[0].contiguous(), root[:1].contiguous()
+    for _ in range(2):
+        out = A.build_tree_sequential(head, h0, s00, r0, D, k, B, wl.beta, wl.T, workspace=ws,
+                                      out=out)
+    torch.cuda.synchronize()
+    trees = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(trees):
+        A.build_tree_sequential(head, h0, s00, r0, D, k, B, wl.beta, wl.T, workspace=ws, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = max(e0.elapsed_time(e1), (time.perf_counter() - w0) * 1e3) / trees
+    n = int(out["n"][0].item())
+    # head calls: the root plus every popped node that is neither the last one nor at depth D
+    depth = out["depth"][:n].cpu().numpy()
+    calls = 1 + int(sum(1 for i in range(n - 1) if depth[i] < D))
+    batched_ms = max(bpm_ms, bpm_wall * 1e3) / steps / wl.R
+    log(f"[bench] sequential best-first: {ms:.2f} ms/tree, {calls} head calls; batched build + "
+        f"prune + mask {batched_ms:.3f} ms/tree ({ms / batched_ms:.2f}x)")
+    return {"ms_per_tree": round(ms, 3), "head_calls": calls, "nodes": n,
+            "batched_ms_per_tree": round(batched_ms, 4), "batched_head_calls": D,
+            "latency_ratio": round(ms / batched_ms, 3)}
 
 
 def cpu_baseline(wl, hw, req, nbuilds):

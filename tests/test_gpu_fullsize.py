@@ -101,3 +101,26 @@ def test_fullsize_tree_attention():
                             f(x["v_tree"]), mask, n, scale)
     assert np.max(np.abs(got - want)) <= 1e-2 * np.max(np.abs(want))
     assert np.linalg.norm(got - want) <= 1e-2 * np.linalg.norm(want)
+
+
+def test_fullsize_sequential_best_first():
+    # the per-node baseline at the Qwen3-4B shape (one head call per expanded
+    # node, B = 64), replayed pop by pop by the fp64 oracle
+    wl = synth.workloads()["qwen3_4b"]
+    print("full-size sequential qwen3_4b", flush=True)
+    hw, req = synth.make_workload_inputs(wl)
+    head = dev_weights(hw, packed=True)
+    h = torch.from_numpy(req.h[0]).to(DEV)
+    s0 = torch.from_numpy(req.s0[0]).to(DEV)
+    root = torch.from_numpy(req.root_tok[:1]).to(DEV)
+    out = to_np(A.build_tree_sequential(head, h, s0, root, wl.D, wl.k, wl.B, wl.beta, wl.T))
+    del head
+    torch.cuda.empty_cache()
+    tol, tau = tolerances(wl.wdtype)
+    from oracle import parity as PAR
+    rep = PAR.check_sequential(oracle_head(hw), req.h[0], req.s0[0], int(req.root_tok[0]), wl.D,
+                               wl.k, wl.B, wl.beta, wl.T, out, tol, tau)
+    assert rep.ok, rep.failures[:5]
+    assert int(out["n"][0]) == wl.B
+    print(f"sequential: exemptions {rep.exemptions} max score err {rep.max_score_err:.3g} "
+          f"head calls {rep.notes[-1]['head_calls']}", flush=True)
