@@ -218,7 +218,9 @@ hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hip
   const int bf = hd->wdtype == DT_BF16, d = hd->d;
   const int packed = hd->layout == DT_LAYOUT_PACKED;
   hipError_t e = hipSuccess;
-  if (bf && io.prep) {
+  // bf16 with few rows: the first product forms x while staging it
+  const bool gather_bf16 = bf && io.prep && w.Mp <= gemm_gather_max_rows();
+  if (bf && io.prep && !gather_bf16) {
     PrepArgs pr;
     pr.E = (const uint16_t*)hd->E;
     pr.d = d;
@@ -236,7 +238,7 @@ hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hip
   GemmArgs g1;
   g1.skip = io.skip;
   g1.pa = PackedA{w.x_hi, w.x_lo, d};
-  g1.a.gather = io.x_dense ? 0 : 1;
+  g1.a.gather = bf ? (gather_bf16 ? 1 : 0) : (io.x_dense ? 0 : 1);
   g1.a.a = io.x_dense;
   g1.a.lda = d;
   g1.a.E = hd->E;

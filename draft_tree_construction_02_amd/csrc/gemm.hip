@@ -95,6 +95,13 @@ extern "C" int dt_trace_read(void* host, size_t bytes) {
 #define DT_MARK(s)
 #endif
 
+// bf16: largest row-tile count whose first product forms x while staging
+// (beyond it a separate kernel writes the x planes first)
+#ifndef DT_GATHER_MAX_MT
+#define DT_GATHER_MAX_MT 2
+#endif
+int gemm_gather_max_rows() { return 16 * DT_GATHER_MAX_MT; }
+
 int gemm_tile_n(int w_bf16) { return w_bf16 ? TN_GEMM : TN_F; }
 int head_tile_n(int w_bf16) { return w_bf16 ? TN_HEAD : TN_F; }
 int head_tiles(const HeadArgs& p) {
@@ -138,6 +145,74 @@ struct AStagePacked {
     for (int i = 0; i < PER_WAVE; ++i) {
       const int bi = wave + i * WV;
       if (NBLK % WV == 0 || bi < NBLK) *(u32x4*)(As + bi * BLK + lane * 8) = v[i];
+    }
+  }
+};
+
+// The first state-update product's activation x = E[tok] + h_t formed while
+// staging (no separate kernel writes x): block pair (mt, kb) of the chunk -
+// the hi and lo blocks of rows 16 mt .. + 15, K 32 kb .. + 31 - is computed
+// by one wave, lane l from E[tok[16 mt + l % 16]] and the row's h at K
+// 32 kb + 8 (l / 16) .. + 8.  Rows >= rows and rows with tok < 0 are zero.
+struct GatherA {
+  ASrc s;
+  int K;
+};
+
+template <int MT, int KC, int WV>
+struct AStageGather {
+  static constexpr int KB = KC / 32;
+  static constexpr int NPAIR = MT * KB;
+  static constexpr int PER_WAVE = (NPAIR + WV - 1) / WV;
+  u32x4 e[PER_WAVE];
+  float4 h0[PER_WAVE], h1[PER_WAVE];
+  int tok[PER_WAVE];
+  bool init = false;
+
+  __device__ __forceinline__ void issue(const GatherA& a, int k) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int bi = wave + i * WV;
+      if (NPAIR % WV == 0 || bi < NPAIR) {
+        const int mt = bi / KB, kb = bi % KB;
+        const int m = 16 * mt + (lane & 15);
+        if (!init) tok[i] = m < a.s.rows ? a.s.tok[m] : -1;
+        const int kk = k + 32 * kb + 8 * (lane >> 4);
+        e[i] = u32x4{0u, 0u, 0u, 0u};
+        h0[i] = h1[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (tok[i] >= 0) {
+          e[i] = *(const u32x4*)((const uint16_t*)a.s.E + (long)tok[i] * a.K + kk);
+          const float* hp = a.s.h + (long)(m / a.s.rpr) * a.s.h_req_stride + kk;
+          h0[i] = *(const float4*)hp;
+          h1[i] = *(const float4*)(hp + 4);
+        }
+      }
+    }
+    init = true;
+  }
+  __device__ __forceinline__ void commit(uint16_t* As) const {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int bi = wave + i * WV;
+      if (NPAIR % WV == 0 || bi < NPAIR) {
+        const int mt = bi / KB, kb = bi % KB;
+        const float y[8] = {bf16_to_f32(e[i][0] & 0xffffu) + h0[i].x, bf16_to_f32(e[i][0] >> 16) + h0[i].y,
+                            bf16_to_f32(e[i][1] & 0xffffu) + h0[i].z, bf16_to_f32(e[i][1] >> 16) + h0[i].w,
+                            bf16_to_f32(e[i][2] & 0xffffu) + h1[i].x, bf16_to_f32(e[i][2] >> 16) + h1[i].y,
+                            bf16_to_f32(e[i][3] & 0xffffu) + h1[i].z, bf16_to_f32(e[i][3] >> 16) + h1[i].w};
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) split_hi_lo(y[j], hi[j], lo[j]);
+        const int blk = mt * KB + kb;
+        *(u32x4*)(As + blk * BLK + lane * 8) =
+            u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16), hi[4] | (hi[5] << 16),
+                  hi[6] | (hi[7] << 16)};
+        *(u32x4*)(As + (MT * KB + blk) * BLK + lane * 8) =
+            u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), lo[4] | (lo[5] << 16),
+                  lo[6] | (lo[7] << 16)};
+      }
     }
   }
 };
@@ -418,7 +493,7 @@ __device__ __forceinline__ float* tile_f32(const ASrc& src, const float* __restr
 // ----------------------------------------------------------------------------
 // split-K partial products
 // ----------------------------------------------------------------------------
-template <int MT, int NBUF, bool PW>
+template <int MT, int NBUF, bool PW, bool GATHER>
 __global__ __launch_bounds__(64 * DT_WV_GEMM) void k_gemm_bf16(GemmArgs g) {
   if (g.skip && *g.skip) return;
   constexpr int NW = DT_NW_GEMM, WV = DT_WV_GEMM;
@@ -429,8 +504,12 @@ __global__ __launch_bounds__(64 * DT_WV_GEMM) void k_gemm_bf16(GemmArgs g) {
   const int klen = g.K / g.splits, k0 = split * klen;
   const int n0 = tile * TN_GEMM;
   f32x4 acc[NW][MT];
-  tile_bf16<MT, NBUF, PW, NW, DT_PF_GEMM, WV, AStagePacked<MT, Cfg::KC, WV>>(
-      g.pa, (const uint16_t*)g.Wt, g.N, n0, k0, klen, smem, acc);
+  if constexpr (GATHER)
+    tile_bf16<MT, NBUF, PW, NW, DT_PF_GEMM, WV, AStageGather<MT, Cfg::KC, WV>>(
+        GatherA{g.a, g.K}, (const uint16_t*)g.Wt, g.N, n0, k0, klen, smem, acc);
+  else
+    tile_bf16<MT, NBUF, PW, NW, DT_PF_GEMM, WV, AStagePacked<MT, Cfg::KC, WV>>(
+        g.pa, (const uint16_t*)g.Wt, g.N, n0, k0, klen, smem, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
 #pragma unroll
@@ -626,10 +705,20 @@ static hipError_t gemm_mt(const GemmArgs& g, hipStream_t st) {
   if (g.w_bf16) {
     constexpr int NB = MT >= DT_NBUF1_MT ? 1 : 2;
     const dim3 blk(64 * DT_WV_GEMM);
-    if (g.w_packed)
-      hipLaunchKernelGGL((k_gemm_bf16<MT, NB, true>), grid, blk, 0, st, g);
-    else
-      hipLaunchKernelGGL((k_gemm_bf16<MT, NB, false>), grid, blk, 0, st, g);
+    if (g.a.gather) {
+      if constexpr (MT <= DT_GATHER_MAX_MT) {
+        if (g.w_packed)
+          hipLaunchKernelGGL((k_gemm_bf16<MT, NB, true, true>), grid, blk, 0, st, g);
+        else
+          hipLaunchKernelGGL((k_gemm_bf16<MT, NB, false, true>), grid, blk, 0, st, g);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    } else if (g.w_packed) {
+      hipLaunchKernelGGL((k_gemm_bf16<MT, NB, true, false>), grid, blk, 0, st, g);
+    } else {
+      hipLaunchKernelGGL((k_gemm_bf16<MT, NB, false, false>), grid, blk, 0, st, g);
+    }
   } else {
     if (g.a.gather)
       hipLaunchKernelGGL((k_gemm_f32<MT, true>), grid, dim3(NT), 0, st, g);

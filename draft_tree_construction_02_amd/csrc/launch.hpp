@@ -75,6 +75,7 @@ struct ReduceArgs {
 };
 
 int gemm_tile_n(int w_bf16);
+int gemm_gather_max_rows();   // bf16: rows up to which x = E[tok] + h is formed in staging
 int gemm_k_chunk(int w_bf16);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 hipError_t launch_reduce(const ReduceArgs& r, hipStream_t st);
