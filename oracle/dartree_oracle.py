@@ -160,10 +160,44 @@ class Supertree:
     lse: list = field(default_factory=list)         # per depth: logsumexp(z/T) of each row
 
 
+def base_candidates(head: OracleHead, h_t: np.ndarray, K: int) -> np.ndarray:
+    """The K candidate tokens of one depth from the drafter's base logits
+    ("Technische Samenvatting: DARTree", Methodologie part 1, Kandidaat
+    Selectie).  Reading: the base logits are h_t U (the drafter hidden of the
+    depth through the same output head); the K best by (logit desc, token
+    asc)."""
+    z = head.logits(np.asarray(h_t, np.float64)[None, :])[0]
+    order = np.lexsort((np.arange(z.size), -z))
+    return order[:K].astype(np.int64)
+
+
+def restricted_children(z: np.ndarray, lp: np.ndarray, cand: np.ndarray, k: int, T: float):
+    """Top-k children of one row among the candidate tokens: by corrected
+    log-probability (full-vocabulary normaliser) desc, token asc.  At T = 0
+    the single child is the lowest-index argmax of z over the candidates, with
+    log-probability 0 (the T -> 0+ limit of the softmax restricted to them)."""
+    cand = np.asarray(cand, np.int64)
+    if T == 0.0:
+        best = cand[np.lexsort((cand, -z[cand]))][0]
+        return np.array([best], np.int64), np.array([0.0])
+    order = np.lexsort((cand, -lp[cand]))[:k]
+    return cand[order], lp[cand[order]]
+
+
 def build_supertree(head: OracleHead, h: np.ndarray, s0: np.ndarray, root_tok: int,
                     D: int, W: int, k: int, T: float,
-                    want_entropy: bool = False) -> Supertree:
-    """Depth-wise batched construction for one request (fp64)."""
+                    want_entropy: bool = False, markov: bool = False,
+                    n_cand: int = 0) -> Supertree:
+    """Depth-wise batched construction for one request (fp64).
+
+    Variants (the pages' head and candidate variants; off by default):
+    * markov: no carried state - every row's update starts from s0, so a
+      node's children depend only on its token and depth (a head without a
+      correction state carried along the branch);
+    * n_cand > 0: each row's children are chosen among the depth's n_cand
+      base-logit candidates (``base_candidates``), scored with the corrected
+      log-probability (``restricted_children``).
+    """
     pool_tok = np.full((D, W), -1, np.int64)
     pool_parent = np.full((D, W), -1, np.int64)
     pool_score = np.full((D, W), NEG_INF)
@@ -176,8 +210,10 @@ def build_supertree(head: OracleHead, h: np.ndarray, s0: np.ndarray, root_tok: i
     for t in range(D):
         # one batched head call over every frontier row
         out.head_calls += 1
-        s_new = state_update(head, f_state, f_tok, h[t])
+        src = np.repeat(np.asarray(s0, np.float64)[None, :], f_tok.size, 0) if markov else f_state
+        s_new = state_update(head, src, f_tok, h[t])
         z = head.logits(s_new)
+        cand_t = base_candidates(head, h[t], n_cand) if n_cand > 0 else None
         cands = []                                    # (score, parent, rank, token)
         ents, lses = [], []
         for i in range(z.shape[0]):
@@ -187,7 +223,10 @@ def build_supertree(head: OracleHead, h: np.ndarray, s0: np.ndarray, root_tok: i
                 lses.append(float(np.max(y) + math.log(np.sum(np.exp(y - np.max(y))))))
                 if want_entropy:
                     ents.append(entropy_T(z[i], T))
-            toks, lps = topk_children(lp, k)
+            if cand_t is None:
+                toks, lps = topk_children(lp, k)
+            else:
+                toks, lps = restricted_children(z[i], lp, cand_t, k, T)
             for r in range(toks.size):
                 cands.append((f_score[i] + lps[r], i, r, int(toks[r])))
         out.entropies.append(ents)

@@ -266,6 +266,95 @@ def test_width_formula_head_calls_and_structure():
             assert np.all(np.isneginf(tree.score[t, n:]))
 
 
+def _paths_with_scores(tree, t):
+    """{token path: score} of the depth-t pool (0-based t)."""
+    out = {}
+    W = tree.tok.shape[1]
+    for j in range(int(tree.n_valid[t])):
+        seq, tt, jj = [], t, j
+        while tt >= 0:
+            seq.append(int(tree.tok[tt, jj]))
+            jj = int(tree.parent[tt, jj]); tt -= 1
+        out[tuple(reversed(seq))] = float(tree.score[t, j])
+    return out
+
+
+def test_markov_width_one_is_the_markov_greedy_chain():
+    # textbook greedy decoding with a head that restarts from s0 every step
+    head = tiny_head(V=40, d=8)
+    h, s0 = _inputs(head, 6)
+    tree = O.build_supertree(head, h, s0, 3, D=6, W=1, k=4, T=1.0, markov=True)
+    tok, score = 3, 0.0
+    for t in range(6):
+        s = O.state_update(head, np.asarray(s0)[None], [tok], h[t])
+        lp = scipy.special.log_softmax(head.logits(s)[0])
+        tok = int(np.argmax(lp))
+        score += lp[tok]
+        assert tree.tok[t, 0] == tok and abs(tree.score[t, 0] - score) < 1e-12
+
+
+def test_markov_children_depend_only_on_token_and_depth():
+    head = tiny_head(V=6, d=8, seed=3)
+    h, s0 = _inputs(head, 3, seed=5)
+    tree = O.build_supertree(head, h, s0, 1, D=3, W=6 ** 3, k=6, T=1.0, markov=True)
+    for t in range(1, 3):
+        seen = {}
+        for j in range(int(tree.n_valid[t])):
+            p = int(tree.parent[t, j])
+            key = (int(tree.tok[t - 1, p]), int(tree.tok[t, j]))
+            lp = float(tree.score[t, j] - tree.score[t - 1, p])
+            if key in seen:
+                assert abs(seen[key] - lp) < 1e-12
+            seen[key] = lp
+    # at depth 3 the same (token, child) pair occurs under many depth-1 tokens
+    assert len(seen) < int(tree.n_valid[2])
+    # a carried-state head does not have this property on the same inputs
+    plain = O.build_supertree(head, h, s0, 1, D=3, W=6 ** 3, k=6, T=1.0)
+    assert not np.allclose(plain.score, tree.score)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.7, 0.0])
+def test_base_candidates_over_the_whole_vocabulary_is_the_plain_build(T):
+    head = tiny_head(V=30, d=8, seed=6)
+    h, s0 = _inputs(head, 4, seed=2)
+    a = O.build_supertree(head, h, s0, 2, D=4, W=7, k=3, T=T)
+    b = O.build_supertree(head, h, s0, 2, D=4, W=7, k=3, T=T, n_cand=30)
+    for x, y in ((a.tok, b.tok), (a.parent, b.parent), (a.n_valid, b.n_valid)):
+        assert np.array_equal(x, y)
+    assert np.array_equal(a.score, b.score)
+
+
+def test_base_candidates_brute_force():
+    # every node's children: the k best of the depth's K base-logit candidates
+    # (np.argsort of h_t U) by scipy's full-vocabulary log_softmax
+    V, D, k, K = 9, 3, 2, 4
+    head = tiny_head(V=V, d=6, seed=9)
+    h, s0 = _inputs(head, D, seed=4)
+    tree = O.build_supertree(head, h, s0, 0, D=D, W=k ** D, k=k, T=1.0, n_cand=K)
+    cands = []
+    for t in range(D):
+        z = head.logits(np.asarray(h[t])[None])[0]
+        cands.append(sorted(range(V), key=lambda c: (-z[c], c))[:K])
+    want = {}
+
+    def rec(state, tok, t, path, score):
+        if t == D:
+            return
+        s = O.state_update(head, np.asarray(state)[None], [tok], h[t])
+        lp = scipy.special.log_softmax(head.logits(s)[0])
+        kids = sorted(cands[t], key=lambda c: (-lp[c], c))[:k]
+        for c in kids:
+            want[path + (c,)] = score + lp[c]
+            rec(s[0], c, t + 1, path + (c,), score + lp[c])
+
+    rec(np.asarray(s0, np.float64), 0, 0, (), 0.0)
+    got = {}
+    for t in range(D):
+        got.update(_paths_with_scores(tree, t))
+    assert got.keys() == want.keys()
+    assert max(abs(got[p] - want[p]) for p in want) < 1e-12
+
+
 def test_survivor_tie_break_on_exact_ties():
     # With E = 0 and h = 0 the update leaves every state equal to s0, so every
     # row has the same children a, b, c with log-probs l0 > l1 > l2.  At depth
