@@ -40,10 +40,13 @@ class Report:
 
 
 def check_build(head, h, s0, root_tok, D, W, k, T, dev, tol, tau,
-                report: Report | None = None) -> Report:
+                report: Report | None = None, markov: bool = False,
+                base_cand: int = 0) -> Report:
     """Check one request's scored pool.
 
     dev: dict with 'tok', 'parent', 'score' ([D][W]) and 'n_valid' ([D]).
+    markov / base_cand select the build variants of ``build_supertree``
+    (base_cand is its n_cand).
     """
     rep = report or Report()
     V = head.V
@@ -54,14 +57,17 @@ def check_build(head, h, s0, root_tok, D, W, k, T, dev, tol, tau,
     f_tok = np.array([root_tok], np.int64)
     f_score = np.array([0.0])
     for t in range(D):
-        s_new = O.state_update(head, f_state, f_tok, h[t])
+        src = np.repeat(np.asarray(s0, np.float64)[None, :], f_tok.size, 0) if markov else f_state
+        s_new = O.state_update(head, src, f_tok, h[t])
         z = head.logits(s_new)
         n_prev = z.shape[0]
+        cand_t = O.base_candidates(head, h[t], base_cand) if base_cand > 0 else None
         lps, kids = [], []
         for i in range(n_prev):
             lp = O.log_softmax_T(z[i], T)
             lps.append(lp)
-            kids.append(O.topk_children(lp, k))
+            kids.append(O.topk_children(lp, k) if cand_t is None
+                        else O.restricted_children(z[i], lp, cand_t, k, T))
         n_cand = sum(kt.size for kt, _ in kids)
         n_exp = min(W, n_cand)
         if int(nv[t]) != n_exp:
@@ -81,6 +87,9 @@ def check_build(head, h, s0, root_tok, D, W, k, T, dev, tol, tau,
             if (p, c) in seen:
                 rep.fail(f"depth {t + 1} slot {j}: duplicate child ({p}, {c})")
             seen.add((p, c))
+            if cand_t is not None and c not in set(cand_t.tolist()):
+                rep.fail(f"depth {t + 1} slot {j}: token {c} is not a base-logit candidate")
+                return rep
             ktoks, klps = kids[p]
             if T == 0.0:
                 # greedy limit: the child must be the argmax up to tau in logit

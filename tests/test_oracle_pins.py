@@ -355,6 +355,21 @@ def test_base_candidates_brute_force():
     assert max(abs(got[p] - want[p]) for p in want) < 1e-12
 
 
+@pytest.mark.parametrize("markov,n_cand", [(True, 0), (False, 8), (True, 6)])
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_build_checker_follows_the_variants(markov, n_cand, T):
+    # the teacher-forced checker accepts a variant's own build and rejects it
+    # as a plain build (the variants are told apart)
+    from oracle import parity as P
+    head = tiny_head(V=50, d=8, seed=0)
+    h, s0 = _inputs(head, 5, seed=1)
+    t = O.build_supertree(head, h, s0, 3, D=5, W=6, k=3, T=T, markov=markov, n_cand=n_cand)
+    dev = dict(tok=t.tok, parent=t.parent, score=t.score, n_valid=t.n_valid)
+    assert P.check_build(head, h, s0, 3, 5, 6, 3, T, dev, 1e-9, 1e-9, markov=markov,
+                         base_cand=n_cand).ok
+    assert not P.check_build(head, h, s0, 3, 5, 6, 3, T, dev, 1e-9, 1e-9).ok
+
+
 def test_survivor_tie_break_on_exact_ties():
     # With E = 0 and h = 0 the update leaves every state equal to s0, so every
     # row has the same children a, b, c with log-probs l0 > l1 > l2.  At depth
