@@ -25,12 +25,20 @@ KERNEL_CLASSES = {"gemm1": 0, "gemm2": 1, "head": 2, "merge_select": 3, "reduce"
 EXPORTS = [
     "dartree_status_string", "dartree_version", "pack_head_bytes", "pack_head",
     "build_supertree_workspace_size", "build_supertree",
+    "build_supertree_ex_workspace_size", "build_supertree_ex",
     "head_step_workspace_size", "state_update", "corrected_topk",
     "build_tree_sequential_workspace_size", "build_tree_sequential",
     "prune_topB", "build_tree_mask",
     "tree_attention_workspace_size", "tree_attention_verify",
     "dartree_timing_enable", "dartree_timing_reset", "dartree_timing_read",
 ]
+
+
+DT_BUILD_MARKOV, DT_BUILD_BASE_CANDIDATES = 1, 2
+
+
+class dt_build_opts(C.Structure):
+    _fields_ = [("flags", C.c_int32), ("n_cand", C.c_int32)]
 
 
 class DartreeError(RuntimeError):
@@ -66,6 +74,10 @@ def lib():
             "build_supertree_workspace_size": (sz, [hp, i32, i32, i32, i32]),
             "build_supertree": (i32, [hp, vp, vp, vp, i32, i32, i32, i32, f32,
                                       vp, vp, vp, vp, vp, sz, vp]),
+            "build_supertree_ex_workspace_size": (sz, [hp, i32, i32, i32, i32,
+                                                       C.POINTER(dt_build_opts)]),
+            "build_supertree_ex": (i32, [hp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                         C.POINTER(dt_build_opts), vp, vp, vp, vp, vp, sz, vp]),
             "head_step_workspace_size": (sz, [hp, i32, i32]),
             "build_tree_sequential_workspace_size": (sz, [hp, i32, i32, i32]),
             "build_tree_sequential": (i32, [hp, vp, vp, vp, i32, i32, i32, f32, f32,
@@ -171,12 +183,22 @@ def build_supertree_workspace_size(head: Head, R, D, W, k) -> int:
     return int(lib().build_supertree_workspace_size(head.ref, R, D, W, k))
 
 
+def _opts(markov: bool, n_cand: int):
+    if not markov and not n_cand:
+        return None
+    return dt_build_opts((DT_BUILD_MARKOV if markov else 0) |
+                         (DT_BUILD_BASE_CANDIDATES if n_cand else 0), int(n_cand))
+
+
 def build_supertree(head: Head, h, s0, root_tok, D: int, W: int, k: int, T: float,
-                    workspace=None, out=None, stream=None) -> dict:
+                    workspace=None, out=None, stream=None, markov: bool = False,
+                    n_cand: int = 0) -> dict:
     """Depth-wise batched supertree construction of R requests.
 
     h [R][D][d] f32, s0 [R][d] f32, root_tok [R] int32 -> dict of pool_tok,
-    pool_parent, pool_score ([R][D][W]) and n_valid ([R][D])."""
+    pool_parent, pool_score ([R][D][W]) and n_valid ([R][D]).  markov / n_cand
+    select the variants of build_supertree_ex (Markov head; children among
+    the depth's n_cand base-logit candidates)."""
     R = s0.shape[0]
     _dev(h, torch.float32, "h", (R, D, head.d))
     _dev(s0, torch.float32, "s0", (R, head.d))
@@ -187,13 +209,25 @@ def build_supertree(head: Head, h, s0, root_tok, D: int, W: int, k: int, T: floa
                    pool_parent=torch.empty((R, D, W), dtype=torch.int32, device=dev),
                    pool_score=torch.empty((R, D, W), dtype=torch.float32, device=dev),
                    n_valid=torch.empty((R, D), dtype=torch.int32, device=dev))
-    need = build_supertree_workspace_size(head, R, D, W, k)
+    opts = _opts(markov, n_cand)
+    if opts is None:
+        need = build_supertree_workspace_size(head, R, D, W, k)
+        ws = _workspace(need, dev, workspace)
+        rc = lib().build_supertree(head.ref, _ptr(h), _ptr(s0), _ptr(root_tok), R, D, W, k,
+                                   float(T), _ptr(out["pool_tok"]), _ptr(out["pool_parent"]),
+                                   _ptr(out["pool_score"]), _ptr(out["n_valid"]), _ptr(ws),
+                                   ws.numel(), _stream(stream))
+        _check(rc, "build_supertree")
+        return out
+    need = int(lib().build_supertree_ex_workspace_size(head.ref, R, D, W, k, C.byref(opts)))
+    if need == 0:
+        raise DartreeError(-1, "build_supertree_ex_workspace_size")
     ws = _workspace(need, dev, workspace)
-    rc = lib().build_supertree(head.ref, _ptr(h), _ptr(s0), _ptr(root_tok), R, D, W, k,
-                               float(T), _ptr(out["pool_tok"]), _ptr(out["pool_parent"]),
-                               _ptr(out["pool_score"]), _ptr(out["n_valid"]), _ptr(ws),
-                               ws.numel(), _stream(stream))
-    _check(rc, "build_supertree")
+    rc = lib().build_supertree_ex(head.ref, _ptr(h), _ptr(s0), _ptr(root_tok), R, D, W, k,
+                                  float(T), C.byref(opts), _ptr(out["pool_tok"]),
+                                  _ptr(out["pool_parent"]), _ptr(out["pool_score"]),
+                                  _ptr(out["n_valid"]), _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "build_supertree_ex")
     return out
 
 

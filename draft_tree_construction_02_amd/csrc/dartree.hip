@@ -388,30 +388,109 @@ size_t build_supertree_workspace_size(const dt_head* head, int R, int D, int W, 
   return c.off;
 }
 
-int build_supertree(const dt_head* head, const float* h, const float* s0, const int32_t* root_tok,
-                    int R, int D, int W, int k, float T, int32_t* pool_tok, int32_t* pool_parent,
-                    float* pool_score, int32_t* n_valid, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+namespace {
+
+struct BuildWs {
+  StepWs w;            // the depth loop (R * W rows)
+  StepWs pre;          // base-candidate pass (chunks of rows of h)
+  int32_t* cand_base;  // [R * D][n_cand]
+  int32_t* msrc;       // Markov residual rows [Mp]
+  int pre_rows;
+};
+
+int build_opts_ok(const dt_head* head, int k, const dt_build_opts* o) {
+  if (!o) return DT_OK;
+  if (o->flags & ~(DT_BUILD_MARKOV | DT_BUILD_BASE_CANDIDATES)) return DT_EINVAL;
+  if (o->flags & DT_BUILD_BASE_CANDIDATES) {
+    if (o->n_cand < k || o->n_cand > head->V) return DT_EINVAL;
+    if (o->n_cand > DT_MAX_K) return DT_EUNSUPPORTED;
+  }
+  return DT_OK;
+}
+
+BuildWs carve_build(Carver& c, const dt_head* head, int R, int D, int W, int k,
+                    const dt_build_opts* o) {
+  BuildWs b{};
+  b.w = carve_step(c, head, R * W, k);
+  const bool base = o && (o->flags & DT_BUILD_BASE_CANDIDATES);
+  if (base) {
+    b.pre_rows = R * D < DT_MAX_ROWS ? R * D : DT_MAX_ROWS;
+    b.pre = carve_step(c, head, b.pre_rows, o->n_cand);
+    b.cand_base = c.take<int32_t>((size_t)R * D * o->n_cand);
+  }
+  if (o && (o->flags & DT_BUILD_MARKOV)) b.msrc = c.take<int32_t>(b.w.Mp);
+  return b;
+}
+
+}  // namespace
+
+size_t build_supertree_ex_workspace_size(const dt_head* head, int R, int D, int W, int k,
+                                         const dt_build_opts* opts) {
+  if (build_args_ok(head, R, D, W, k) != DT_OK || build_opts_ok(head, k, opts) != DT_OK)
+    return 0;
+  Carver c(nullptr);
+  carve_build(c, head, R, D, W, k, opts);
+  return c.off;
+}
+
+int build_supertree_ex(const dt_head* head, const float* h, const float* s0,
+                       const int32_t* root_tok, int R, int D, int W, int k, float T,
+                       const dt_build_opts* opts, int32_t* pool_tok, int32_t* pool_parent,
+                       float* pool_score, int32_t* n_valid, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   int rc = build_args_ok(head, R, D, W, k);
+  if (rc != DT_OK) return rc;
+  rc = build_opts_ok(head, k, opts);
   if (rc != DT_OK) return rc;
   if (!h || !s0 || !root_tok || !pool_tok || !pool_parent || !pool_score || !n_valid)
     return DT_EINVAL;
   if (!(T >= 0.f) || !isfinite(T)) return DT_EINVAL;
-  const size_t need = build_supertree_workspace_size(head, R, D, W, k);
+  const size_t need = build_supertree_ex_workspace_size(head, R, D, W, k, opts);
   if (!workspace || workspace_bytes < need) return DT_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   Carver c(workspace);
-  StepWs w = carve_step(c, head, R * W, k);
+  BuildWs bw = carve_build(c, head, R, D, W, k, opts);
+  const StepWs& w = bw.w;
   const int d = head->d, rows = R * W;
-  const bool greedy = T == 0.f;
+  const bool greedy = T == 0.f, bf = head->wdtype == DT_BF16;
+  const bool markov = opts && (opts->flags & DT_BUILD_MARKOV);
+  const bool base = opts && (opts->flags & DT_BUILD_BASE_CANDIDATES);
+  const int n_cand = base ? opts->n_cand : 0;
 
-  hipError_t e = launch_beam_init(R, W, w.Mp, root_tok, w.tok[0], w.score[0], w.src[0], st);
+  hipError_t e = hipSuccess;
+  if (base) {
+    // candidates of every (request, depth): the top n_cand of h_t U, in
+    // chunks of rows of h
+    for (int c0 = 0; c0 < R * D && e == hipSuccess; c0 += bw.pre_rows) {
+      const int rc_rows = R * D - c0 < bw.pre_rows ? R * D - c0 : bw.pre_rows;
+      const float* hs = h + (long)c0 * d;
+      if (bf) {
+        ReduceArgs r;
+        r.part = hs;
+        r.splits = 1;
+        r.Mp = bw.pre.Mp;
+        r.N = d;
+        r.rows = rc_rows;
+        r.rows_out = 0;
+        r.epi = EPI_RESID;
+        r.out_hi = bw.pre.s_hi;
+        r.out_lo = bw.pre.s_lo;
+        e = launch_reduce(r, st);
+      }
+      if (e == hipSuccess)
+        e = run_head(head, bw.pre, hs, rc_rows, n_cand, 1.f, bw.cand_base + (long)c0 * n_cand,
+                     bw.pre.cand_lp, bw.pre.lse, st);
+    }
+  }
+  if (markov && e == hipSuccess) e = launch_markov_src(rows, W, w.Mp, bw.msrc, st);
+  if (e == hipSuccess)
+    e = launch_beam_init(R, W, w.Mp, root_tok, w.tok[0], w.score[0], w.src[0], st);
   for (int t = 0; t < D && e == hipSuccess; ++t) {
     const int cur = t & 1, nxt = cur ^ 1;
     DepthIo io;
-    io.s_prev = t == 0 ? s0 : w.S[nxt];
+    io.s_prev = (t == 0 || markov) ? s0 : w.S[nxt];
     io.tok = w.tok[cur];
-    io.src = w.src[cur];
+    io.src = markov ? bw.msrc : w.src[cur];
     io.h = h + (long)t * d;
     io.h_req_stride = (long)D * d;
     io.rpr = W;
@@ -420,12 +499,35 @@ int build_supertree(const dt_head* head, const float* h, const float* s0, const 
     io.rows_out = rows;
     e = run_update(head, w, io, st);
     if (e != hipSuccess) break;
-    e = run_head(head, w, w.S[cur], rows, k, T, w.cand_tok, w.cand_lp, w.lse, st, false);
+    // base candidates: the full merge gives each row's log-sum-exp, then the
+    // children are chosen among the depth's candidates
+    e = run_head(head, w, w.S[cur], rows, k, T, w.cand_tok, w.cand_lp, w.lse, st, base);
     if (e != hipSuccess) break;
+    if (base) {
+      CandArgs ca;
+      ca.s = w.S[cur];
+      ca.lse = w.lse;
+      ca.cand_base = bw.cand_base;
+      ca.Ut = head->Ut;
+      ca.u_bf16 = bf;
+      ca.u_packed = head->layout == DT_LAYOUT_PACKED;
+      ca.d = d; ca.W = W; ca.D = D; ca.t = t; ca.n_cand = n_cand; ca.k = k;
+      ca.greedy = greedy;
+      ca.inv_T = greedy ? 1.f : (float)(1.0 / (double)T);
+      ca.cand_tok = w.cand_tok;
+      ca.cand_lp = w.cand_lp;
+      e = timed(DT_K_MERGE, st, [&] { return launch_cand_score(ca, rows, st); });
+      if (e != hipSuccess) break;
+    }
     BeamArgs b;
     b.R = R; b.W = W; b.k = k; b.D = D; b.t = t; b.greedy = greedy;
-    b.ms2 = w.ms2;
-    b.key2 = w.key2;
+    if (base) {
+      b.cand_tok = w.cand_tok;
+      b.cand_lp = w.cand_lp;
+    } else {
+      b.ms2 = w.ms2;
+      b.key2 = w.key2;
+    }
     b.S = merge_splits(head_tiles_for(head, w.Mp));
     b.kmax = kmax_for(k, greedy);
     b.score_in = w.score[cur];
@@ -440,6 +542,14 @@ int build_supertree(const dt_head* head, const float* h, const float* s0, const 
     e = timed(DT_K_MERGE, st, [&] { return launch_beam_step(b, st); });
   }
   return e == hipSuccess ? DT_OK : DT_EHIP;
+}
+
+int build_supertree(const dt_head* head, const float* h, const float* s0, const int32_t* root_tok,
+                    int R, int D, int W, int k, float T, int32_t* pool_tok, int32_t* pool_parent,
+                    float* pool_score, int32_t* n_valid, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return build_supertree_ex(head, h, s0, root_tok, R, D, W, k, T, nullptr, pool_tok, pool_parent,
+                            pool_score, n_valid, workspace, workspace_bytes, stream);
 }
 
 size_t head_step_workspace_size(const dt_head* head, int rows, int k) {

@@ -143,6 +143,10 @@ hipError_t launch_pack_weight(const uint16_t* src, uint16_t* dst, int N, int K, 
 // Beam bookkeeping for one depth of R requests.
 struct BeamArgs {
   int R = 0, W = 0, k = 0, D = 0, t = 0, greedy = 0;
+  // children per row: either the merge range results (ms2 / key2) folded
+  // here, or (ms2 == nullptr) already chosen in cand_tok / cand_lp [Mp][k]
+  const int32_t* cand_tok = nullptr;
+  const float* cand_lp = nullptr;
   const float2* ms2 = nullptr;         // merge range results [Mp][S]
   const uint64_t* key2 = nullptr;      // [Mp][S][kmax]
   int S = 1, kmax = 1;
@@ -158,6 +162,21 @@ struct BeamArgs {
 };
 hipError_t launch_beam_init(int R, int W, int Mp, const int32_t* root_tok, int32_t* tok,
                             float* score, int32_t* src, hipStream_t st);
+// Base-candidate variant: children of each row among its depth's candidates.
+struct CandArgs {
+  const float* s = nullptr;            // updated states [rows][d] f32
+  const float* lse = nullptr;          // [rows] logsumexp(z / T)
+  const int32_t* cand_base = nullptr;  // [R * D][n_cand]
+  const void* Ut = nullptr;
+  int u_bf16 = 1, u_packed = 0;
+  int d = 0, W = 1, D = 1, t = 0, n_cand = 1, k = 1, greedy = 0;
+  float inv_T = 1.f;
+  int32_t* cand_tok = nullptr;         // [rows][k]
+  float* cand_lp = nullptr;
+};
+hipError_t launch_cand_score(const CandArgs& a, int rows, hipStream_t st);
+hipError_t launch_markov_src(int rows, int W, int Mp, int32_t* src, hipStream_t st);
+
 // Children of every frontier row from the merge range results, then the
 // global top-W step.
 hipError_t launch_beam_step(const BeamArgs& b, hipStream_t st);

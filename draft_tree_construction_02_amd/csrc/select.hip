@@ -257,9 +257,18 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_step(BeamArgs b) {
   const int ncand_max = b.W * keff;
   int32_t* c_tok = (int32_t*)(keys + ncand_max);           // [ncand]
 
+  if (!b.ms2) {
+    // children already chosen per row (cand_tok / cand_lp, stride k)
+    for (int c = tid; c < ncand; c += BEAM_THREADS) {
+      const int i = c / keff, j = c % keff;
+      const long o = (long)(base + i) * b.k + j;
+      c_tok[c] = b.cand_tok[o];
+      keys[c] = make_key(b.score_in[base + i] + b.cand_lp[o], (uint32_t)c);
+    }
+  }
   int S2 = 1;
   while (S2 < b.S) S2 <<= 1;
-  for (int i = wave; i < n_prev; i += BEAM_THREADS / 64) {
+  for (int i = wave; b.ms2 && i < n_prev; i += BEAM_THREADS / 64) {
     const long o = (long)(base + i) * b.S + lane;
     MaxSum tot{-INFINITY, 0.f};
     TopK<KMAX> all;
@@ -325,6 +334,111 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_step(BeamArgs b) {
       b.score_out[j] = -INFINITY;
       b.src_out[j] = -1;
     }
+}
+
+// Markov variant: every row's residual source is its request's s0 row.
+__global__ void k_markov_src(int rows, int W, int Mp, int32_t* src) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < Mp) src[i] = i < rows ? i / W : -1;
+}
+
+hipError_t launch_markov_src(int rows, int W, int Mp, int32_t* src, hipStream_t st) {
+  hipLaunchKernelGGL(k_markov_src, dim3((Mp + 255) / 256), dim3(256), 0, st, rows, W, Mp, src);
+  return hipGetLastError();
+}
+
+// Output-head row c, columns kk .. kk + 7, as floats (kk % 8 == 0).
+__device__ __forceinline__ void u_row8(const CandArgs& a, int c, int kk, float (&u)[8]) {
+  if (!a.u_bf16) {
+    const float* p = (const float*)a.Ut + (long)c * a.d + kk;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[e] = p[e];
+    return;
+  }
+  const uint16_t* p;
+  if (a.u_packed) {
+    // grouped packed layout: block (g, kb, t), lane (c % 16) + 16 ((kk % 32) / 8)
+    constexpr int TPG = PACK_ROWS / 16;
+    const int tile = c / 16;
+    const int lane = (c & 15) + 16 * ((kk & 31) >> 3);
+    p = (const uint16_t*)a.Ut +
+        ((((long)(tile / TPG) * (a.d / 32) + kk / 32) * TPG + tile % TPG) * 512 + lane * 8);
+  } else {
+    p = (const uint16_t*)a.Ut + (long)c * a.d + kk;
+  }
+  const u32x4 v = *(const u32x4*)p;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    u[2 * e] = bf16_to_f32(v[e] & 0xffffu);
+    u[2 * e + 1] = bf16_to_f32(v[e] >> 16);
+  }
+}
+
+// Base-candidate variant: one workgroup per row i.  z_c = s'_i . U[c] for
+// the depth's n_cand candidates (fp32), logp_c = z_c / T - lse_i, and the
+// row's k best candidates by (logp desc, token asc); T == 0: the
+// lowest-index argmax of z over the candidates, logp 0.
+__global__ __launch_bounds__(256) void k_cand_score(CandArgs a) {
+  __shared__ float zc[DT_MAX_K];
+  const int i = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = i / a.W;
+  const int32_t* cand = a.cand_base + ((long)r * a.D + a.t) * a.n_cand;
+  const float* s = a.s + (long)i * a.d;
+  for (int q = wave; q < a.n_cand; q += 4) {
+    const int c = cand[q];
+    float acc = 0.f;
+    for (int kk = lane * 8; kk < a.d; kk += 64 * 8) {
+      float u[8];
+      u_row8(a, c, kk, u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf(s[kk + e], u[e], acc);
+    }
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) zc[q] = acc;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  int32_t* ot = a.cand_tok + (long)i * a.k;
+  float* ol = a.cand_lp + (long)i * a.k;
+  for (int j = 0; j < a.k; ++j) {
+    ot[j] = -1;
+    ol[j] = -INFINITY;
+  }
+  if (a.greedy) {
+    int best = -1;
+    float bz = -INFINITY;
+    for (int q = 0; q < a.n_cand; ++q) {
+      const int c = cand[q];
+      if (best < 0 || zc[q] > bz || (zc[q] == bz && c < best)) {
+        best = c;
+        bz = zc[q];
+      }
+    }
+    ot[0] = best;
+    ol[0] = 0.f;
+    return;
+  }
+  // insertion of the candidates into a (logp desc, token asc) list of k
+  int nt = 0;
+  for (int q = 0; q < a.n_cand; ++q) {
+    const int c = cand[q];
+    const float lp = zc[q] * a.inv_T - a.lse[i];
+    int pos = nt;
+    while (pos > 0 && (lp > ol[pos - 1] || (lp == ol[pos - 1] && c < ot[pos - 1]))) --pos;
+    if (pos >= a.k) continue;
+    for (int m = (nt < a.k ? nt : a.k - 1); m > pos; --m) {
+      ot[m] = ot[m - 1];
+      ol[m] = ol[m - 1];
+    }
+    ot[pos] = c;
+    ol[pos] = lp;
+    if (nt < a.k) ++nt;
+  }
+}
+
+hipError_t launch_cand_score(const CandArgs& a, int rows, hipStream_t st) {
+  hipLaunchKernelGGL(k_cand_score, dim3(rows), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_beam_step(const BeamArgs& b, hipStream_t st) {

@@ -165,6 +165,43 @@ int build_supertree(const dt_head* head, const float* h, const float* s0,
                     int32_t* n_valid, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Build variants (dt_build_opts.flags). */
+#define DT_BUILD_MARKOV 1           /* no carried state: every update starts from s0    */
+#define DT_BUILD_BASE_CANDIDATES 2  /* children only among the depth's base candidates   */
+
+typedef struct {
+  int32_t flags;    /* DT_BUILD_* bits                                                   */
+  int32_t n_cand;   /* DT_BUILD_BASE_CANDIDATES: candidates per depth, k <= n_cand <= DT_MAX_K */
+} dt_build_opts;
+
+/* Device bytes of workspace build_supertree_ex needs (0 if invalid). */
+size_t build_supertree_ex_workspace_size(const dt_head* head, int R, int D, int W, int k,
+                                         const dt_build_opts* opts);
+
+/*
+ * build_supertree_ex - build_supertree with the variants the pages discuss
+ * (opts == NULL or flags == 0: exactly build_supertree).
+ *  - DT_BUILD_MARKOV: a Markov correction head that carries no state along
+ *    the branch (the DSpark drafter of [P2] Experimentele Resultaten,
+ *    Generaliseerbaarheid): every row's update
+ *    is s' = s0[r] + GELU((E[tok] + h_t) W1) W2, so a node's children depend
+ *    on its token and depth only.
+ *  - DT_BUILD_BASE_CANDIDATES: at each depth the n_cand candidate tokens are
+ *    the top of the drafter's base logits, read here as h_t U (by logit desc,
+ *    token asc), shared by the request's branches ([P2] part 1, Kandidaat
+ *    Selectie); each branch's children are its k best candidates by the
+ *    corrected log-probability (full-vocabulary normaliser), token asc on
+ *    ties.  T == 0: the single child is the lowest-index argmax of z over the
+ *    candidates, logp 0.  The candidates of all D depths come from one extra
+ *    head pass over the R*D hidden rows before the depth loop.
+ * Arguments and outputs as build_supertree; opts is a host pointer.
+ */
+int build_supertree_ex(const dt_head* head, const float* h, const float* s0,
+                       const int32_t* root_tok, int R, int D, int W, int k, float T,
+                       const dt_build_opts* opts, int32_t* pool_tok, int32_t* pool_parent,
+                       float* pool_score, int32_t* n_valid, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Stages of one depth (the same kernels build_supertree runs)               */
 /* ------------------------------------------------------------------------ */

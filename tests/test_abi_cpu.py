@@ -26,7 +26,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     L = A.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -106,6 +106,28 @@ def test_build_tree_sequential_validation():
     assert seq(h, ws=10) == DT_EWORKSPACE
     assert seq(h, wsp=None) == DT_EWORKSPACE
     assert seq(fake_head(V=4), k=8) == DT_EINVAL
+
+
+def test_build_supertree_ex_validation():
+    L = A.lib()
+    h = fake_head()
+    o = A.dt_build_opts(A.DT_BUILD_MARKOV, 0)
+    assert L.build_supertree_ex_workspace_size(C.byref(h), 1, 16, 16, 8, C.byref(o)) > 0
+    assert L.build_supertree_ex_workspace_size(C.byref(h), 1, 16, 16, 8, None) == \
+        L.build_supertree_workspace_size(C.byref(h), 1, 16, 16, 8)
+
+    def ex(opts, **kw):
+        p = dict(k=8, T=1.0, ws=1 << 40)
+        p.update(kw)
+        return L.build_supertree_ex(C.byref(h), 1, 1, 1, 1, 16, 16, p["k"], p["T"],
+                                    C.byref(opts) if opts is not None else None, 1, 1, 1, 1, 1,
+                                    p["ws"], None)
+    assert ex(A.dt_build_opts(8, 0)) == DT_EINVAL                        # unknown flag
+    assert ex(A.dt_build_opts(A.DT_BUILD_BASE_CANDIDATES, 4)) == DT_EINVAL   # n_cand < k
+    assert ex(A.dt_build_opts(A.DT_BUILD_BASE_CANDIDATES, 17)) == DT_EUNSUPPORTED
+    assert ex(A.dt_build_opts(A.DT_BUILD_MARKOV, 0), T=-1.0) == DT_EINVAL
+    assert ex(A.dt_build_opts(A.DT_BUILD_MARKOV, 0), ws=10) == DT_EWORKSPACE
+    assert ex(None, k=0) == DT_EINVAL
 
 
 def test_pack_head_validation():
