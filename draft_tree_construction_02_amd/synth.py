@@ -18,6 +18,10 @@ Recipe (stated once, used everywhere):
   h multiplied by ``h_scale``).
 * Verification stream ``spawn(5)``: q, k_prefix, v_prefix, k_tree, v_tree,
   N(0,1).
+* Target stream ``root.spawn(4)[3]`` (the first three children are the ones
+  above): the synthetic greedy target of the acceptance walk shares E, W1t
+  and W2t with the draft head and has Ut + sigma * (3/sqrt(d)) * N(0,1) as
+  its output matrix, drawn like Ut and rounded to the storage type.
 * bf16 storage is float32 rounded to nearest, ties to even, on the bit pattern.
 
 The head follows the synthetic correction-head recipe of the workloads:
@@ -208,6 +212,20 @@ def make_verify_inputs(n_tree: int, P: int, Hq: int, Hkv: int, hd: int,
         k_tree=bf16_bits(_normal(kt_ss, n_tree * Hkv * hd, 1.0).reshape(n_tree, Hkv, hd)),
         v_tree=bf16_bits(_normal(vt_ss, n_tree * Hkv * hd, 1.0).reshape(n_tree, Hkv, hd)),
     )
+
+
+def make_target(head: HeadWeights, sigma: float, seed: int = 0) -> HeadWeights:
+    """Synthetic target for the acceptance walk: the draft head with its output
+    matrix perturbed by N(0, (sigma * 3/sqrt(d))^2) noise (see header)."""
+    tss = np.random.SeedSequence(seed).spawn(4)[3]
+    noise = _normal(tss, head.V * head.d, sigma * 3.0 / math.sqrt(head.d)).reshape(head.V, head.d)
+    if head.wdtype == "bf16":
+        noise += bf16_bits_to_f32(head.Ut)
+        Ut = bf16_bits(noise)
+    else:
+        noise += head.Ut
+        Ut = noise
+    return HeadWeights(head.wdtype, head.V, head.d, head.E, head.W1t, head.W2t, Ut)
 
 
 def make_workload_inputs(wl: Workload):

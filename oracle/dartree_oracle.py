@@ -192,8 +192,9 @@ def build_supertree(head: OracleHead, h: np.ndarray, s0: np.ndarray, root_tok: i
 
     Variants (the pages' head and candidate variants; off by default):
     * markov: no carried state - every row's update starts from s0, so a
-      node's children depend only on its token and depth (a head without a
-      correction state carried along the branch);
+      node's children depend only on its token and depth (a Markov
+      correction head, as in the DSpark drafter of "Technische Samenvatting:
+      DARTree", Experimentele Resultaten, Generaliseerbaarheid);
     * n_cand > 0: each row's children are chosen among the depth's n_cand
       base-logit candidates (``base_candidates``), scored with the corrected
       log-probability (``restricted_children``).
@@ -378,6 +379,69 @@ def sequential_best_first(head: OracleHead, h: np.ndarray, s0: np.ndarray, root_
     n = len(out_tok)
     return SeqTree(np.array(out_tok, np.int64), np.array(out_par, np.int64),
                    np.array(out_depth, np.int64), np.array(out_score, np.float64), n, calls)
+
+
+# ----------------------------------------------------------------------------
+# acceptance walk against a synthetic target (verification stand-in)
+# ----------------------------------------------------------------------------
+@dataclass
+class Walk:
+    target_tok: np.ndarray   # [B + 1]: target's greedy token after the root (0) and node i (1 + i);
+                             # -1 for nodes without children
+    path: list               # accepted node indices, depth 1, 2, ...
+    tau: int                 # tokens per verification round = len(path) + 1
+
+
+def acceptance_walk(target: OracleHead, h: np.ndarray, s0: np.ndarray, root_tok: int,
+                    tok, parent, depth, n: int, D: int, B: int) -> Walk:
+    """Verify one draft tree against a synthetic greedy target.
+
+    "DARTree: Teaching a Chain-Trained Corrector to Think in Trees": Core
+    Mechanism (the target checks the whole tree in one forward and keeps the
+    longest prefix it agrees with), Key Concepts (tokens accepted per
+    verification round), Expert Assessment (compare trees of matched size).
+
+    The pages' target is a language model; the stand-in is a chain model of
+    the correction head's form with weights of its own (``target``).  Its
+    state after a node follows the node's path from the root:
+    s'_root = s0 + step(root_tok, h[0]), s'_v = s'_parent(v) + step(tok_v,
+    h[depth(v)]), the draft head's recurrence, and its greedy token
+    after v is the lowest-index argmax of s'_v U_target.  The target's token
+    is needed only after nodes that have children.
+
+    The walk starts at the root; while the current node has a child whose
+    token is the target's token after it, it moves to that child (the
+    lowest-index one if several match); it stops at a node with no such
+    child.  tau counts the accepted draft tokens plus the target's own token
+    after the last of them.  Tree: node i < n has token tok[i], parent
+    parent[i] (-1: the root) earlier in the list and depth depth[i] =
+    depth of the parent + 1, at most D.
+    """
+    tok = np.asarray(tok)[:n]; parent = np.asarray(parent)[:n]; depth = np.asarray(depth)[:n]
+    has_child = np.zeros(n + 1, bool)                 # slot 0: the root
+    for i in range(n):
+        has_child[int(parent[i]) + 1] = True
+    states = {-1: state_update(target, np.asarray(s0, np.float64)[None, :], [int(root_tok)],
+                               h[0])[0]}
+    target_tok = np.full(B + 1, -1, np.int64)
+    if has_child[0]:
+        target_tok[0] = int(np.argmax(target.logits(states[-1][None, :])[0]))
+    for i in range(n):
+        if not has_child[i + 1]:
+            continue
+        states[i] = state_update(target, states[int(parent[i])][None, :], [int(tok[i])],
+                                 h[int(depth[i])])[0]
+        target_tok[i + 1] = int(np.argmax(target.logits(states[i][None, :])[0]))
+    path, cur, dcur = [], -1, 0
+    while dcur < D and target_tok[cur + 1] >= 0:
+        want = int(target_tok[cur + 1])
+        match = [i for i in range(n) if int(parent[i]) == cur and int(tok[i]) == want]
+        if not match:
+            break
+        cur = match[0]
+        dcur = int(depth[cur])
+        path.append(cur)
+    return Walk(target_tok, path, len(path) + 1)
 
 
 # ----------------------------------------------------------------------------

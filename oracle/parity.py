@@ -302,3 +302,65 @@ def check_sequential(head, h, s0, root_tok, D, k, B, beta, T, dev, tol, tau) -> 
         rep.fail(f"n = {n} > B")
     rep.notes.append(dict(head_calls=len(row_lp)))
     return rep
+
+
+def check_walk(target, h, s0, root_tok, D, B, tree, dev, tau) -> Report:
+    """Check a device acceptance walk of one tree against the synthetic target.
+
+    tree: dict of tok, parent, depth ([>= n]) and n.  dev: dict of target_tok
+    ([B + 1]), path ([D]) and accept_len.  Every target token the device
+    reports is compared with the fp64 argmax of the target's logits at that
+    node (a different token passes only when its fp64 logit is within tau of
+    the maximum, counted as an exemption); nodes without children must report
+    -1.  The walk is then replayed on the device's target tokens and must
+    equal the device's path exactly.
+    """
+    rep = Report()
+    n = int(tree["n"])
+    tok = np.asarray(tree["tok"])[:n]; par = np.asarray(tree["parent"])[:n]
+    dep = np.asarray(tree["depth"])[:n]
+    tt = np.asarray(dev["target_tok"]).reshape(-1)
+    has_child = np.zeros(B + 1, bool)
+    for i in range(n):
+        has_child[int(par[i]) + 1] = True
+    states = {-1: O.state_update(target, np.asarray(s0, np.float64)[None, :], [int(root_tok)],
+                                 h[0])[0]}
+    for j in range(B + 1):
+        i = j - 1
+        if i >= 0 and has_child[j]:
+            states[i] = O.state_update(target, states[int(par[i])][None, :], [int(tok[i])],
+                                       h[int(dep[i])])[0]
+        if not has_child[j]:
+            if int(tt[j]) != -1:
+                rep.fail(f"entry {i}: target token {tt[j]} for a node without children")
+            continue
+        z = target.logits(states[i][None, :])[0]
+        best = int(np.argmax(z))
+        got = int(tt[j])
+        if got == best:
+            continue
+        if not 0 <= got < z.size:
+            rep.fail(f"entry {i}: target token {got} out of range")
+            continue
+        gap = float(z[best] - z[got])
+        if gap <= tau:
+            rep.exemptions += 1
+        else:
+            rep.fail(f"entry {i}: target token {got} vs argmax {best} (gap {gap:.3g})")
+    # the walk over the device's target tokens
+    path, cur = [], -1
+    while len(path) < D and int(tt[cur + 1]) >= 0:
+        want = int(tt[cur + 1])
+        match = [i for i in range(n) if int(par[i]) == cur and int(tok[i]) == want]
+        if not match:
+            break
+        cur = match[0]
+        path.append(cur)
+    got_path = [int(x) for x in np.asarray(dev["path"]).reshape(-1)]
+    want_path = path + [-1] * (D - len(path))
+    if got_path != want_path:
+        rep.fail(f"path {got_path} vs {want_path}")
+    if int(np.asarray(dev["accept_len"]).reshape(-1)[0]) != len(path):
+        rep.fail(f"accept_len {dev['accept_len']} vs {len(path)}")
+    rep.notes.append(dict(tau=len(path) + 1))
+    return rep

@@ -508,6 +508,138 @@ def test_sequential_T0_is_the_greedy_chain():
 
 
 # ----------------------------------------------------------------------------
+# acceptance walk against a synthetic target
+# ----------------------------------------------------------------------------
+def _perturbed(head, sigma, seed):
+    """A target sharing E, W1, W2 with `head`, U perturbed (float32 storage)."""
+    g = np.random.default_rng(seed)
+    Ut = (head._Ut + sigma * g.standard_normal(head._Ut.shape)).astype(np.float32)
+    return O.OracleHead("f32", head._E, head.W1.T.astype(np.float32),
+                        head.W2.T.astype(np.float32), Ut)
+
+
+def _state_from_scratch(head, h, s0, root, path_toks):
+    """State after a token sequence, recomputed position by position."""
+    s = np.asarray(s0, np.float64)[None]
+    for j, t in enumerate([root] + list(path_toks)):
+        s = O.state_update(head, s, [t], h[j])
+    return s[0]
+
+
+def test_walk_with_the_draft_head_as_target_accepts_the_whole_greedy_chain():
+    head = tiny_head(V=40, d=8)
+    D = 6
+    h, s0 = _inputs(head, D)
+    toks, _ = _greedy_chain(head, h, s0, 3, D)
+    seq = O.sequential_best_first(head, h, s0, 3, D=D, k=4, B=D, beta=0.0, T=0.0)
+    w = O.acceptance_walk(head, h, s0, 3, seq.tok, seq.parent, seq.depth, seq.n, D, B=D)
+    assert w.tau == D + 1 and w.path == list(range(D))
+    # the target's token after each chain node is the next chain token; the
+    # depth-D leaf has no children and no target token
+    assert w.target_tok.tolist() == toks + [-1]
+
+
+@settings(max_examples=15, deadline=None)
+@given(seed=st.integers(0, 60), sigma=st.sampled_from([0.05, 0.3, 1.0]),
+       kind=st.sampled_from(["sequential", "pruned"]))
+def test_walk_is_the_longest_tree_prefix_of_the_target_greedy_continuation(seed, sigma, kind):
+    D, k, B = 4, 3, 14
+    head = tiny_head(V=9, d=6, seed=seed)
+    target = _perturbed(head, sigma, seed + 1)
+    h, s0 = _inputs(head, D, seed=seed + 200)
+    if kind == "sequential":
+        t = O.sequential_best_first(head, h, s0, 1, D=D, k=k, B=B, beta=-0.2, T=1.0)
+        tok, par, dep, n = t.tok, t.parent, t.depth, t.n
+    else:
+        W = 5
+        tr = O.build_supertree(head, h, s0, 1, D=D, W=W, k=k, T=1.0)
+        vt = O.prune_topB(tr.score, tr.parent, tr.n_valid, B, -0.2)
+        n = vt.n
+        tok = np.array([tr.tok[int(x) // W, int(x) % W] for x in vt.node[:n]], np.int64)
+        par, dep = vt.parent[:n], vt.depth[:n]
+    w = O.acceptance_walk(target, h, s0, 1, tok, par, dep, n, D, B)
+    # independent formulation: the target decodes greedily from the root; tau
+    # is 1 + the longest prefix of that continuation that is a root path
+    g, _ = _greedy_chain(target, h, s0, 1, D)
+    paths = {}
+    for i in range(n):
+        p, j = [], i
+        while j >= 0:
+            p.append(int(tok[j])); j = int(par[j])
+        paths[tuple(reversed(p))] = i
+    L = 0
+    while L < D and tuple(g[:L + 1]) in paths:
+        L += 1
+    assert w.tau == L + 1
+    assert [int(tok[i]) for i in w.path] == g[:L]
+    assert [paths[tuple(g[:j + 1])] for j in range(L)] == w.path
+    # target token of every node with children, from the state recomputed along
+    # its token sequence
+    kids = {int(p) for p in par}
+    for i in range(n):
+        if i not in kids:
+            assert w.target_tok[i + 1] == -1
+            continue
+        seqtoks = [int(tok[x]) for x in _seq_ancestry(par, i)]
+        s = _state_from_scratch(target, h, s0, 1, seqtoks)
+        assert w.target_tok[i + 1] == int(np.argmax(target.logits(s[None])[0]))
+    assert w.target_tok[0] == (g[0] if n else -1)
+    assert np.all(w.target_tok[n + 1:] == -1)
+
+
+def _seq_ancestry(par, i):
+    out = []
+    while i >= 0:
+        out.append(i); i = int(par[i])
+    return list(reversed(out))
+
+
+def test_walk_edge_cases():
+    head = tiny_head(V=9, d=6, seed=4)
+    D, B = 3, 5
+    h, s0 = _inputs(head, D)
+    empty = O.acceptance_walk(head, h, s0, 2, [], [], [], 0, D, B)
+    assert empty.tau == 1 and empty.path == [] and np.all(empty.target_tok == -1)
+    g, _ = _greedy_chain(head, h, s0, 2, D)
+    wrong = (g[0] + 1) % 9
+    # a root child that is not the target's token stops the walk at once
+    w = O.acceptance_walk(head, h, s0, 2, [wrong], [-1], [1], 1, D, B)
+    assert w.tau == 1 and w.target_tok[0] == g[0] and w.target_tok[1] == -1
+    # the matching child is found among siblings, whatever its position
+    w = O.acceptance_walk(head, h, s0, 2, [wrong, g[0], g[1]], [-1, -1, 1], [1, 1, 2], 3, D, B)
+    assert w.path == [1, 2] and w.tau == 3
+    assert w.target_tok.tolist()[:3] == [g[0], -1, g[1]]
+
+
+def test_walk_checker_accepts_the_oracle_and_rejects_planted_mistakes():
+    from oracle import parity as P
+    head = tiny_head(V=30, d=8, seed=5)
+    target = _perturbed(head, 0.1, 9)
+    D, k, B = 4, 3, 12
+    h, s0 = _inputs(head, D, seed=6)
+    t = O.sequential_best_first(head, h, s0, 2, D=D, k=k, B=B, beta=0.0, T=1.0)
+    tree = dict(tok=t.tok, parent=t.parent, depth=t.depth, n=t.n)
+    w = O.acceptance_walk(target, h, s0, 2, t.tok, t.parent, t.depth, t.n, D, B)
+    assert w.tau >= 2          # the seed is chosen so that the walk goes somewhere
+    path = np.array(w.path + [-1] * (D - len(w.path)))
+    dev = dict(target_tok=w.target_tok.copy(), path=path, accept_len=[len(w.path)])
+    assert P.check_walk(target, h, s0, 2, D, B, tree, dev, 1e-9).ok
+    inner = [j for j in range(B + 1) if w.target_tok[j] >= 0]
+    for mut in ("target", "leaf", "path", "len"):
+        bad = {kk: np.array(v).copy() for kk, v in dev.items()}
+        if mut == "target":
+            bad["target_tok"][inner[-1]] = (bad["target_tok"][inner[-1]] + 1) % 30
+        elif mut == "leaf":
+            leaf = [j for j in range(1, t.n + 1) if w.target_tok[j] < 0][0]
+            bad["target_tok"][leaf] = 0
+        elif mut == "path":
+            bad["path"][0] = (bad["path"][0] + 1) % t.n
+        else:
+            bad["accept_len"][0] += 1
+        assert not P.check_walk(target, h, s0, 2, D, B, tree, bad, 1e-9).ok, mut
+
+
+# ----------------------------------------------------------------------------
 # deferred pruning (Lemma 1), ancestor closure, mask
 # ----------------------------------------------------------------------------
 def test_prune_and_mask_hand_examples():
