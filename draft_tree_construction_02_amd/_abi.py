@@ -30,6 +30,7 @@ EXPORTS = [
     "build_tree_sequential_workspace_size", "build_tree_sequential",
     "prune_topB", "build_tree_mask",
     "tree_attention_workspace_size", "tree_attention_verify",
+    "accept_walk_workspace_size", "accept_walk",
     "dartree_timing_enable", "dartree_timing_reset", "dartree_timing_read",
 ]
 
@@ -89,6 +90,9 @@ def lib():
             "tree_attention_workspace_size": (sz, [i32, i32, i32, i32, i32]),
             "tree_attention_verify": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                             f32, vp, vp, sz, vp]),
+            "accept_walk_workspace_size": (sz, [hp, i32, i32, i32]),
+            "accept_walk": (i32, [hp, vp, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp,
+                                  vp, vp, vp, vp, sz, vp]),
             "dartree_timing_enable": (i32, [i32]),
             "dartree_timing_reset": (i32, []),
             "dartree_timing_read": (i32, [i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
@@ -346,6 +350,51 @@ def tree_attention_verify(q, k_prefix, v_prefix, k_tree, v_tree, mask, scale: fl
                                      float(scale), _ptr(out), _ptr(ws), ws.numel(),
                                      _stream(stream))
     _check(rc, "tree_attention_verify")
+    return out
+
+
+def accept_walk_workspace_size(target: Head, R, D, B) -> int:
+    return int(lib().accept_walk_workspace_size(target.ref, R, D, B))
+
+
+def accept_walk(target: Head, h, s0, root_tok, tok, parent, depth, n, tok_index=None,
+                workspace=None, out=None, stream=None) -> dict:
+    """Acceptance walk of R draft trees against the synthetic greedy target
+    `target` (a head of its own).
+
+    h [R][D][d] f32, s0 [R][d] f32, root_tok [R] i32; parent, depth [R][B]
+    i32; n [R] i32; tok [R][B] i32, or with tok_index [R][B] i32 any
+    [R][stride] i32 that tok_index indexes (build_supertree's pool_tok as
+    [R][D*W] with prune_topB's sel_node).  Returns a dict of target_tok
+    [R][B+1], path [R][D] and accept_len [R] (tokens per round = accept_len + 1).
+    """
+    R, D = h.shape[0], h.shape[1]
+    B = parent.shape[1]
+    _dev(h, torch.float32, "h", (R, D, target.d))
+    _dev(s0, torch.float32, "s0", (R, target.d))
+    _dev(root_tok, torch.int32, "root_tok", (R,))
+    _dev(parent, torch.int32, "parent", (R, B))
+    _dev(depth, torch.int32, "depth", (R, B))
+    _dev(n, torch.int32, "n", (R,))
+    if tok_index is None:
+        _dev(tok, torch.int32, "tok", (R, B))
+    else:
+        _dev(tok_index, torch.int32, "tok_index", (R, B))
+        _dev(tok, torch.int32, "tok")
+        if tok.dim() != 2 or tok.shape[0] != R:
+            raise ValueError("tok must be [R][stride]")
+    dev = h.device
+    if out is None:
+        out = dict(target_tok=torch.empty((R, B + 1), dtype=torch.int32, device=dev),
+                   path=torch.empty((R, D), dtype=torch.int32, device=dev),
+                   accept_len=torch.empty((R,), dtype=torch.int32, device=dev))
+    need = accept_walk_workspace_size(target, R, D, B)
+    ws = _workspace(need, dev, workspace)
+    rc = lib().accept_walk(target.ref, _ptr(h), _ptr(s0), _ptr(root_tok), R, D, B, _ptr(tok),
+                           int(tok.shape[1]), _ptr(tok_index), _ptr(parent), _ptr(depth),
+                           _ptr(n), _ptr(out["target_tok"]), _ptr(out["path"]),
+                           _ptr(out["accept_len"]), _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "accept_walk")
     return out
 
 

@@ -744,6 +744,126 @@ int build_tree_sequential(const dt_head* head, const float* h, const float* s0,
   return e == hipSuccess ? DT_OK : DT_EHIP;
 }
 
+// ---------------------------------------------------------------- acceptance walk
+struct WalkWs {
+  StepWs step;                 // one chunk of CH rows, greedy keys
+  WalkArgs a;
+  float* S[2];                 // updated states of depth t (ping-pong) [nch * CH][d]
+  uint64_t* key2_all;          // merge range results of every chunk
+};
+
+static WalkWs carve_walk(Carver& c, const dt_head* h, int R, int D, int B) {
+  WalkWs w{};
+  const int nodes = R * B;
+  const int CH = padded_rows(nodes < DT_MAX_ROWS ? nodes : DT_MAX_ROWS);
+  w.step = carve_step(c, h, CH, 1);
+  WalkArgs& a = w.a;
+  a.R = R; a.D = D; a.B = B; a.V = h->V; a.d = h->d;
+  a.CH = CH;
+  a.nch = (nodes + CH - 1) / CH;
+  a.bf16 = h->wdtype == DT_BF16;
+  a.S = merge_splits(head_tiles_for(h, CH));
+  const size_t rows = (size_t)a.nch * CH, d = h->d, B1 = (size_t)B + 1;
+  if (a.bf16) {
+    a.x_hi = c.take<uint16_t>(rows * d);
+    a.x_lo = c.take<uint16_t>(rows * d);
+  } else {
+    a.x_f32 = c.take<float>(rows * d);
+  }
+  w.S[0] = c.take<float>(rows * d);
+  w.S[1] = c.take<float>(rows * d);
+  w.key2_all = c.take<uint64_t>(rows * a.S);
+  a.key2 = w.key2_all;
+  a.has_child = c.take<uint8_t>((size_t)R * B1);
+  a.pos = c.take<int32_t>((size_t)R * B1);
+  a.row_req = c.take<int32_t>(rows);
+  a.row_node = c.take<int32_t>(rows);
+  a.row_tok = c.take<int32_t>(rows);
+  a.row_src = c.take<int32_t>(rows);
+  a.ctl = c.take<int32_t>(1);
+  a.skip = c.take<int32_t>(a.nch);
+  return w;
+}
+
+static int walk_args_ok(const dt_head* target, int R, int D, int B) {
+  if (!head_ok(target)) return DT_EINVAL;
+  if (R < 1 || D < 1 || B < 1) return DT_EINVAL;
+  if (D > DT_MAX_DEPTH || B > DT_MAX_B || (long)R * B > DT_MAX_WALK_NODES)
+    return DT_EUNSUPPORTED;
+  return DT_OK;
+}
+
+size_t accept_walk_workspace_size(const dt_head* target, int R, int D, int B) {
+  if (walk_args_ok(target, R, D, B) != DT_OK) return 0;
+  Carver c(nullptr);
+  carve_walk(c, target, R, D, B);
+  return c.off;
+}
+
+int accept_walk(const dt_head* target, const float* h, const float* s0, const int32_t* root_tok,
+                int R, int D, int B, const int32_t* tok, int tok_stride,
+                const int32_t* tok_index, const int32_t* parent, const int32_t* depth,
+                const int32_t* n, int32_t* target_tok, int32_t* path, int32_t* accept_len,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = walk_args_ok(target, R, D, B);
+  if (rc != DT_OK) return rc;
+  if (!h || !s0 || !root_tok || !tok || !parent || !depth || !n || !target_tok || !path ||
+      !accept_len)
+    return DT_EINVAL;
+  if (tok_stride < (tok_index ? 1 : B)) return DT_EINVAL;
+  const size_t need = accept_walk_workspace_size(target, R, D, B);
+  if (!workspace || workspace_bytes < need) return DT_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  Carver c(workspace);
+  WalkWs ww = carve_walk(c, target, R, D, B);
+  WalkArgs& a = ww.a;
+  a.root_tok = root_tok;
+  a.tok = tok;
+  a.tok_stride = tok_stride;
+  a.tok_index = tok_index;
+  a.parent = parent;
+  a.depth = depth;
+  a.n = n;
+  a.E = target->E;
+  a.h = h;
+  a.target_tok = target_tok;
+  a.path = path;
+  a.accept_len = accept_len;
+  const int d = target->d, CH = a.CH;
+  hipError_t e = timed(DT_K_MERGE, st, [&] { return launch_walk_init(a, st); });
+  for (int t = 0; t < D && e == hipSuccess; ++t) {
+    e = timed(DT_K_MERGE, st, [&] { return launch_walk_rows(a, t, st); });
+    for (int ch = 0; ch < a.nch && e == hipSuccess; ++ch) {
+      StepWs wc = ww.step;
+      if (a.bf16) {
+        wc.x_hi = a.x_hi + (size_t)ch * CH * d;
+        wc.x_lo = a.x_lo + (size_t)ch * CH * d;
+      }
+      wc.key2 = ww.key2_all + (size_t)ch * CH * a.S;
+      DepthIo io;
+      io.s_prev = t == 0 ? s0 : ww.S[(t - 1) & 1];
+      io.tok = nullptr;
+      io.src = a.row_src + (size_t)ch * CH;
+      io.h = nullptr;
+      io.h_req_stride = 0;
+      io.rpr = 1;
+      io.rows = CH;
+      io.s_out = ww.S[t & 1] + (size_t)ch * CH * d;
+      io.rows_out = CH;
+      io.skip = a.skip + ch;
+      io.prep = false;
+      io.x_dense = a.bf16 ? nullptr : a.x_f32 + (size_t)ch * CH * d;
+      e = run_update(target, wc, io, st);
+      if (e == hipSuccess)
+        e = run_head(target, wc, io.s_out, CH, 1, 0.f, nullptr, nullptr, nullptr, st, false,
+                     io.skip);
+    }
+  }
+  if (e == hipSuccess) e = timed(DT_K_MERGE, st, [&] { return launch_walk_rows(a, D, st); });
+  if (e == hipSuccess) e = timed(DT_K_MERGE, st, [&] { return launch_walk(a, st); });
+  return e == hipSuccess ? DT_OK : DT_EHIP;
+}
+
 int prune_topB(const float* pool_score, const int32_t* pool_parent, const int32_t* n_valid, int R,
                int D, int W, int B, float beta, int32_t* sel_node, int32_t* sel_parent,
                int32_t* sel_depth, int32_t* n_sel, void* stream) {

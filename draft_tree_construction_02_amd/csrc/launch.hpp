@@ -227,6 +227,42 @@ hipError_t launch_seq_init(const SeqArgs& a, const float* s0, const int32_t* roo
                            hipStream_t st);
 hipError_t launch_seq_step(const SeqArgs& a, int slot, hipStream_t st);
 
+// Acceptance walk (verify.hip).  Rows of one depth are the tree nodes of that
+// depth that have children, compacted over all requests in (request, node)
+// order and evaluated in chunks of CH rows; ctl[0] holds the row count.
+struct WalkArgs {
+  int R = 0, D = 0, B = 0, V = 0, d = 0, CH = 0, nch = 0, S = 1, bf16 = 1;
+  const int32_t* root_tok = nullptr;   // [R]
+  const int32_t* tok = nullptr;        // node tokens, see node_token
+  int tok_stride = 0;
+  const int32_t* tok_index = nullptr;  // [R][B] or null
+  const int32_t* parent = nullptr;     // [R][B]
+  const int32_t* depth = nullptr;      // [R][B]
+  const int32_t* n = nullptr;          // [R]
+  const void* E = nullptr;             // target embedding (bf16 or fp32)
+  const float* h = nullptr;            // [R][D][d]
+  int32_t* target_tok = nullptr;       // [R][B + 1]
+  int32_t* path = nullptr;             // [R][D]
+  int32_t* accept_len = nullptr;       // [R]
+  uint8_t* has_child = nullptr;        // [R][B + 1], slot 0 = root
+  int32_t* pos = nullptr;              // [R][B + 1] row of the node at its depth
+  int32_t* row_req = nullptr;          // [nch * CH]
+  int32_t* row_node = nullptr;         // node index, -1 = root
+  int32_t* row_tok = nullptr;
+  int32_t* row_src = nullptr;          // residual row (previous depth's rows; s0 row at depth 0)
+  int32_t* ctl = nullptr;              // [1] rows of the current depth
+  int32_t* skip = nullptr;             // [nch] chunk flags
+  const uint64_t* key2 = nullptr;      // merge range results [nch][CH][S] (greedy keys)
+  uint16_t* x_hi = nullptr;            // bf16: packed x planes [nch][CH][d]
+  uint16_t* x_lo = nullptr;
+  float* x_f32 = nullptr;              // fp32: dense x [nch * CH][d]
+};
+hipError_t launch_walk_init(const WalkArgs& a, hipStream_t st);
+// Scatter the target tokens of depth t - 1 (t > 0), then (t < D) compact the
+// rows of depth t and write their x.
+hipError_t launch_walk_rows(const WalkArgs& a, int t, hipStream_t st);
+hipError_t launch_walk(const WalkArgs& a, hipStream_t st);
+
 // Runs fn(ctx) bracketed by timing events of kernel class cls when kernel
 // timing is on (dartree_timing_enable).
 hipError_t timed_launch(int cls, hipStream_t st, hipError_t (*fn)(void*), void* ctx);

@@ -333,6 +333,57 @@ int tree_attention_verify(const void* q, const void* k_prefix, const void* v_pre
                           void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Acceptance walk against a synthetic greedy target                         */
+/* ------------------------------------------------------------------------ */
+
+#define DT_MAX_WALK_NODES 8192   /* R * B: draft nodes per accept_walk call */
+
+/* Device bytes of workspace accept_walk needs (0 if the arguments are invalid). */
+size_t accept_walk_workspace_size(const dt_head* target, int R, int D, int B);
+
+/*
+ * accept_walk - verification of R draft trees by a synthetic greedy target
+ * ([P1] Core Mechanism: one target forward checks every branch and the
+ * longest agreeing prefix is kept; [P1] Key Concepts: accepted tokens per
+ * verification round; [P1] Expert Assessment: compare trees of matched size).
+ * The pages' target is a language model; here it is a chain model of the
+ * correction head's form with its own weights (`target`, any dt_head).  Its
+ * state after node v follows v's path: s'(root) = s0 + step(root_tok, h row 0),
+ * s'(v) = s'(parent v) + step(tok v, h row depth(v)), with
+ * step(t, x) = GELU((E[t] + x) W1) W2, and its token after v is the
+ * lowest-index argmax of s'(v) U.  It is evaluated depth by depth, once for
+ * every node that has children, in batches of up to 128 rows (the same
+ * state-update and head kernels as the builds, T == 0).
+ * The walk starts at the root and moves to the child (lowest index first)
+ * whose token is the target's token after the current node, until no child
+ * matches; tokens per round = accept_len + 1.
+ * Tree of request r (device arrays, row stride B): n[r] nodes (clamped to
+ * [0, B]); node i has parent parent[r][i] (-1: child of the root) with
+ * parent < i, depth depth[r][i] = depth of the parent + 1 (1..D), token
+ *   tok[r * tok_stride + i]                       when tok_index == NULL,
+ *   tok[r * tok_stride + tok_index[r * B + i]]    otherwise
+ * (so prune_topB's sel_node indexes build_supertree's pool_tok directly,
+ * tok_stride = D * W; the sequential tree is tok_stride = B, no index).
+ * Nodes that break these rules, have a token outside [0, V) or an index
+ * outside [0, tok_stride) get no target token and are never accepted.
+ *   h [R][D][d] f32, s0 [R][d] f32, root_tok [R] i32.
+ * Outputs:
+ *   target_tok [R][B + 1] i32  target's token after the root (column 0) and
+ *                              after node i (column 1 + i); -1 where the node
+ *                              has no children
+ *   path       [R][D] i32      accepted nodes in depth order, then -1
+ *   accept_len [R] i32         accepted draft nodes
+ * 1 <= R, 1 <= B <= DT_MAX_B, R * B <= DT_MAX_WALK_NODES,
+ * 1 <= D <= DT_MAX_DEPTH; everything runs on `stream`.
+ */
+int accept_walk(const dt_head* target, const float* h, const float* s0,
+                const int32_t* root_tok, int R, int D, int B, const int32_t* tok,
+                int tok_stride, const int32_t* tok_index, const int32_t* parent,
+                const int32_t* depth, const int32_t* n, int32_t* target_tok,
+                int32_t* path, int32_t* accept_len, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Kernel timing (off by default)                                            */
 /* ------------------------------------------------------------------------ */
 

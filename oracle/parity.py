@@ -325,16 +325,22 @@ def check_walk(target, h, s0, root_tok, D, B, tree, dev, tau) -> Report:
         has_child[int(par[i]) + 1] = True
     states = {-1: O.state_update(target, np.asarray(s0, np.float64)[None, :], [int(root_tok)],
                                  h[0])[0]}
+    inner = []
     for j in range(B + 1):
         i = j - 1
-        if i >= 0 and has_child[j]:
-            states[i] = O.state_update(target, states[int(par[i])][None, :], [int(tok[i])],
-                                       h[int(dep[i])])[0]
         if not has_child[j]:
             if int(tt[j]) != -1:
                 rep.fail(f"entry {i}: target token {tt[j]} for a node without children")
             continue
-        z = target.logits(states[i][None, :])[0]
+        if i >= 0:
+            states[i] = O.state_update(target, states[int(par[i])][None, :], [int(tok[i])],
+                                       h[int(dep[i])])[0]
+        inner.append(j)
+    # one pass over the target's output matrix for every node with children
+    Z = target.logits(np.stack([states[j - 1] for j in inner])) if inner else None
+    for q, j in enumerate(inner):
+        i = j - 1
+        z = Z[q]
         best = int(np.argmax(z))
         got = int(tt[j])
         if got == best:

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     L = A.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -106,6 +106,38 @@ def test_build_tree_sequential_validation():
     assert seq(h, ws=10) == DT_EWORKSPACE
     assert seq(h, wsp=None) == DT_EWORKSPACE
     assert seq(fake_head(V=4), k=8) == DT_EINVAL
+
+
+def walk(hd, R=1, D=16, B=64, stride=64, index=None, ws=1 << 40, wsp=1, **kw):
+    p = dict(hid=1, s0=1, root=1, tok=1, par=1, depth=1, n=1, tt=1, path=1, alen=1)
+    p.update(kw)
+    return A.lib().accept_walk(C.byref(hd), p["hid"], p["s0"], p["root"], R, D, B, p["tok"],
+                               stride, index, p["par"], p["depth"], p["n"], p["tt"], p["path"],
+                               p["alen"], wsp, ws, None)
+
+
+def test_accept_walk_validation():
+    h = fake_head()
+    L = A.lib()
+    assert L.accept_walk_workspace_size(C.byref(h), 1, 16, 64) > 0
+    assert L.accept_walk_workspace_size(C.byref(h), 0, 16, 64) == 0
+    assert L.accept_walk_workspace_size(C.byref(h), 8, 16, 1025) == 0
+    # the workspace grows with the number of nodes
+    assert L.accept_walk_workspace_size(C.byref(h), 8, 16, 128) > \
+        L.accept_walk_workspace_size(C.byref(h), 1, 16, 128)
+    assert walk(h, R=0) == DT_EINVAL
+    assert walk(h, D=0) == DT_EINVAL
+    assert walk(h, B=0) == DT_EINVAL
+    assert walk(h, B=1025, stride=1025) == DT_EUNSUPPORTED
+    assert walk(h, R=9, B=1024, stride=1024) == DT_EUNSUPPORTED     # R * B > 8192
+    assert walk(h, D=65) == DT_EUNSUPPORTED
+    assert walk(h, stride=63) == DT_EINVAL                           # row of B tokens
+    assert walk(h, stride=0, index=1) == DT_EINVAL
+    for name in ("hid", "s0", "root", "tok", "par", "depth", "n", "tt", "path", "alen"):
+        assert walk(h, **{name: None}) == DT_EINVAL, name
+    assert walk(h, ws=10) == DT_EWORKSPACE
+    assert walk(h, wsp=None) == DT_EWORKSPACE
+    assert walk(fake_head(d=2500)) == DT_EINVAL
 
 
 def test_build_supertree_ex_validation():

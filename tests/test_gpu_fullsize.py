@@ -124,3 +124,44 @@ def test_fullsize_sequential_best_first():
     assert int(out["n"][0]) == wl.B
     print(f"sequential: exemptions {rep.exemptions} max score err {rep.max_score_err:.3g} "
           f"head calls {rep.notes[-1]['head_calls']}", flush=True)
+
+
+def test_fullsize_acceptance_walk_matched_size():
+    # the Qwen3-4B-shaped supertree (pruned to B = 64) and the sequential tree
+    # of the same budget, both verified by the synthetic target (the draft
+    # head with U perturbed, sigma 0.1) on the device and checked node by
+    # node in fp64
+    wl = synth.workloads()["qwen3_4b"]
+    print("full-size acceptance walk qwen3_4b", flush=True)
+    hw, req = synth.make_workload_inputs(wl)
+    thw = synth.make_target(hw, 0.1, wl.weight_seed)
+    head, thead = dev_weights(hw, packed=True), dev_weights(thw, packed=True)
+    h, s0, root = dev_requests(req)
+    out = A.build_supertree(head, h, s0, root, wl.D, wl.W, wl.k, wl.T)
+    sel = A.prune_topB(out["pool_score"], out["pool_parent"], out["n_valid"], wl.B, wl.beta)
+    wb = to_np(A.accept_walk(thead, h, s0, root, out["pool_tok"].reshape(1, -1),
+                             sel["sel_parent"], sel["sel_depth"], sel["n_sel"],
+                             tok_index=sel["sel_node"]))
+    seq = A.build_tree_sequential(head, h[0], s0[0], root, wl.D, wl.k, wl.B, wl.beta, wl.T)
+    wsq = to_np(A.accept_walk(thead, h, s0, root, seq["tok"][None], seq["parent"][None],
+                              seq["depth"][None], seq["n"]))
+    pool_tok = out["pool_tok"].cpu().numpy().reshape(-1)
+    sn, sq = to_np(sel), to_np(seq)
+    del head, thead, out, sel, seq
+    torch.cuda.empty_cache()
+    n_b, n_s = int(sn["n_sel"][0]), int(sq["n"][0])
+    assert n_b == n_s == wl.B                     # matched verification-tree size
+    _, tau = tolerances(wl.wdtype)
+    otarget = oracle_head(thw)
+    from oracle import parity as PAR
+    taus = []
+    for tree, w in ((dict(tok=pool_tok[sn["sel_node"][0][:n_b]], parent=sn["sel_parent"][0],
+                          depth=sn["sel_depth"][0], n=n_b), wb),
+                    (dict(tok=sq["tok"], parent=sq["parent"], depth=sq["depth"], n=n_s), wsq)):
+        dev = dict(target_tok=w["target_tok"][0], path=w["path"][0], accept_len=w["accept_len"])
+        rep = PAR.check_walk(otarget, req.h[0], req.s0[0], int(req.root_tok[0]), wl.D, wl.B,
+                             tree, dev, tau)
+        assert rep.ok, rep.failures[:5]
+        taus.append((rep.notes[-1]["tau"], rep.exemptions))
+    print(f"tokens per round at B={wl.B}: batched {taus[0][0]}, sequential {taus[1][0]} "
+          f"(exemptions {taus[0][1]}, {taus[1][1]})", flush=True)
