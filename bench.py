@@ -11,7 +11,10 @@ Prints one JSON line.  `value` is supertree builds per second (R per step).
 The roofline object reports the corrected-logit head kernel: algorithmic
 bytes per launch (2 d V, the bf16 output head streamed once) divided by its
 average launch time measured with HIP events on the launch stream.
-The cpu_baseline object times the fp64 oracle on a bounded sample.
+The cpu_baseline object times the fp64 oracle on a bounded sample.  Outside
+the timed step: sequential_baseline (one head call per expanded node, same
+budget) and acceptance (tokens per round of the pruned trees, and of the
+sequential tree, under a synthetic greedy target; the walk's own time).
 
   python bench.py [--steps K] [--warmup W] [--workload qwen3_4b]
 """
@@ -67,6 +70,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sequential", action="store_true",
                     help="skip the sequential best-first (one head call per node) comparison")
+    ap.add_argument("--no-walk", action="store_true",
+                    help="skip the acceptance walk against the synthetic target")
     ap.add_argument("--cpu-builds", type=int, default=1,
                     help="oracle builds timed for cpu_baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -247,9 +252,13 @@ def main():
         "step_weight_stream_gbs": round(bytes_per_step / (ms_per_step * 1e-3) / 1e9, 1),
     }
 
+    seq_tree = None
     if wl.R == 1 and not args.no_sequential:
-        res["sequential_baseline"] = sequential_baseline(A, head, h, s0, root, wl, b_ms, b_wall,
-                                                         bpm_ms, bpm_wall, args.steps)
+        res["sequential_baseline"], seq_tree = sequential_baseline(A, head, h, s0, root, wl, b_ms,
+                                                                   b_wall, bpm_ms, bpm_wall,
+                                                                   args.steps)
+    if not args.no_walk:
+        res["acceptance"] = acceptance(A, synth, hw, wl, up, h, s0, root, pool, sel, seq_tree)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, hw, req, args.cpu_builds)
     print(json.dumps(res), flush=True)
@@ -286,9 +295,59 @@ def sequential_baseline(A, head, h, s0, root, wl, b_ms, b_wall, bpm_ms, bpm_wall
     batched_ms = max(bpm_ms, bpm_wall * 1e3) / steps / wl.R
     log(f"[bench] sequential best-first: {ms:.2f} ms/tree, {calls} head calls; batched build + "
         f"prune + mask {batched_ms:.3f} ms/tree ({ms / batched_ms:.2f}x)")
-    return {"ms_per_tree": round(ms, 3), "head_calls": calls, "nodes": n,
-            "batched_ms_per_tree": round(batched_ms, 4), "batched_head_calls": D,
-            "latency_ratio": round(ms / batched_ms, 3)}
+    return ({"ms_per_tree": round(ms, 3), "head_calls": calls, "nodes": n,
+             "batched_ms_per_tree": round(batched_ms, 4), "batched_head_calls": D,
+             "latency_ratio": round(ms / batched_ms, 3)}, out)
+
+
+TARGET_SIGMA = 0.1
+
+
+def acceptance(A, synth, hw, wl, up, h, s0, root, pool, sel, seq_tree):
+    """Tokens per verification round of the step's pruned trees (and of the
+    sequential tree of the same budget B, one request) under the synthetic
+    greedy target: the draft head with its output matrix perturbed.  Not part
+    of the timed step; the walk itself is timed separately."""
+    import torch
+    t0 = time.time()
+    thw = synth.make_target(hw, TARGET_SIGMA, wl.weight_seed)
+    target = A.Head(up(thw.E), up(thw.W1t), up(thw.W2t), up(thw.Ut))
+    if wl.wdtype == "bf16":
+        target = target.packed()
+    torch.cuda.synchronize()
+    R, D, W, B = wl.R, wl.D, wl.W, wl.B
+    ws = torch.empty(A.accept_walk_workspace_size(target, R, D, B), dtype=torch.uint8,
+                     device="cuda:0")
+
+    def walk_pool(out=None):
+        return A.accept_walk(target, h, s0, root, pool["pool_tok"].view(R, D * W),
+                             sel["sel_parent"], sel["sel_depth"], sel["n_sel"],
+                             tok_index=sel["sel_node"], workspace=ws, out=out)
+    out = walk_pool()
+    torch.cuda.synchronize()
+    reps = 5
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        walk_pool(out)
+    e1.record()
+    torch.cuda.synchronize()
+    walk_ms = e0.elapsed_time(e1) / reps
+    tau_b = [int(x) + 1 for x in out["accept_len"].cpu().tolist()]
+    res = {"target": f"draft head with U + N(0, ({TARGET_SIGMA} * 3/sqrt(d))^2), greedy",
+           "B": B, "nodes_batched": [int(x) for x in sel["n_sel"].cpu().tolist()],
+           "tau_batched": tau_b, "walk_ms": round(walk_ms, 3)}
+    if seq_tree is not None:
+        wsq = A.accept_walk(target, h, s0, root, seq_tree["tok"][None], seq_tree["parent"][None],
+                            seq_tree["depth"][None], seq_tree["n"])
+        res["nodes_sequential"] = int(seq_tree["n"][0].item())
+        res["tau_sequential"] = int(wsq["accept_len"][0].item()) + 1
+    log(f"[bench] acceptance walk ({time.time() - t0:.1f}s incl. target): tokens/round "
+        f"batched {tau_b}" + (f", sequential {res['tau_sequential']}" if seq_tree is not None
+                              else "") + f"; walk {walk_ms:.2f} ms")
+    del target
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(wl, hw, req, nbuilds):
