@@ -749,7 +749,7 @@ struct WalkWs {
   StepWs step;                 // one chunk of CH rows, greedy keys
   WalkArgs a;
   float* S[2];                 // updated states of depth t (ping-pong) [nch * CH][d]
-  uint64_t* key2_all;          // merge range results of every chunk
+  uint64_t* key2_all;          // merge range results of every inner-node chunk
 };
 
 static WalkWs carve_walk(Carver& c, const dt_head* h, int R, int D, int B) {
@@ -777,10 +777,13 @@ static WalkWs carve_walk(Carver& c, const dt_head* h, int R, int D, int B) {
   a.has_child = c.take<uint8_t>((size_t)R * B1);
   a.pos = c.take<int32_t>((size_t)R * B1);
   a.row_req = c.take<int32_t>(rows);
-  a.row_node = c.take<int32_t>(rows);
   a.row_tok = c.take<int32_t>(rows);
   a.row_src = c.take<int32_t>(rows);
-  a.ctl = c.take<int32_t>(1);
+  a.row_gidx = c.take<int32_t>(rows);
+  a.inner_req = c.take<int32_t>(rows);
+  a.inner_node = c.take<int32_t>(rows);
+  a.S_inner = c.take<float>(rows * d);
+  a.ctl = c.take<int32_t>(2);
   a.skip = c.take<int32_t>(a.nch);
   return w;
 }
@@ -831,6 +834,7 @@ int accept_walk(const dt_head* target, const float* h, const float* s0, const in
   a.accept_len = accept_len;
   const int d = target->d, CH = a.CH;
   hipError_t e = timed(DT_K_MERGE, st, [&] { return launch_walk_init(a, st); });
+  // the target's states, depth by depth, filed under the inner-node list
   for (int t = 0; t < D && e == hipSuccess; ++t) {
     e = timed(DT_K_MERGE, st, [&] { return launch_walk_rows(a, t, st); });
     for (int ch = 0; ch < a.nch && e == hipSuccess; ++ch) {
@@ -839,7 +843,6 @@ int accept_walk(const dt_head* target, const float* h, const float* s0, const in
         wc.x_hi = a.x_hi + (size_t)ch * CH * d;
         wc.x_lo = a.x_lo + (size_t)ch * CH * d;
       }
-      wc.key2 = ww.key2_all + (size_t)ch * CH * a.S;
       DepthIo io;
       io.s_prev = t == 0 ? s0 : ww.S[(t - 1) & 1];
       io.tok = nullptr;
@@ -854,12 +857,35 @@ int accept_walk(const dt_head* target, const float* h, const float* s0, const in
       io.prep = false;
       io.x_dense = a.bf16 ? nullptr : a.x_f32 + (size_t)ch * CH * d;
       e = run_update(target, wc, io, st);
-      if (e == hipSuccess)
-        e = run_head(target, wc, io.s_out, CH, 1, 0.f, nullptr, nullptr, nullptr, st, false,
-                     io.skip);
     }
+    if (e == hipSuccess)
+      e = timed(DT_K_MERGE, st, [&] { return launch_walk_keep(a, ww.S[t & 1], st); });
   }
+  // one pass of the target's head over every inner node
   if (e == hipSuccess) e = timed(DT_K_MERGE, st, [&] { return launch_walk_rows(a, D, st); });
+  for (int ch = 0; ch < a.nch && e == hipSuccess; ++ch) {
+    StepWs wc = ww.step;
+    wc.key2 = ww.key2_all + (size_t)ch * CH * a.S;
+    const float* s_rows = a.S_inner + (size_t)ch * CH * d;
+    if (a.bf16) {
+      // split the fp32 states into the packed hi/lo planes
+      ReduceArgs r;
+      r.skip = a.skip + ch;
+      r.part = s_rows;
+      r.splits = 1;
+      r.Mp = CH;
+      r.N = d;
+      r.rows = CH;
+      r.rows_out = 0;
+      r.epi = EPI_RESID;
+      r.out_hi = wc.s_hi;
+      r.out_lo = wc.s_lo;
+      e = timed(DT_K_REDUCE, st, [&] { return launch_reduce(r, st); });
+    }
+    if (e == hipSuccess)
+      e = run_head(target, wc, s_rows, CH, 1, 0.f, nullptr, nullptr, nullptr, st, false,
+                   a.skip + ch);
+  }
   if (e == hipSuccess) e = timed(DT_K_MERGE, st, [&] { return launch_walk(a, st); });
   return e == hipSuccess ? DT_OK : DT_EHIP;
 }

@@ -229,7 +229,9 @@ hipError_t launch_seq_step(const SeqArgs& a, int slot, hipStream_t st);
 
 // Acceptance walk (verify.hip).  Rows of one depth are the tree nodes of that
 // depth that have children, compacted over all requests in (request, node)
-// order and evaluated in chunks of CH rows; ctl[0] holds the row count.
+// order and evaluated in chunks of CH rows; ctl[0] holds the row count of the
+// current depth, ctl[1] the number of inner nodes listed so far (all depths,
+// in depth order: inner_req / inner_node, their states in S_inner).
 struct WalkArgs {
   int R = 0, D = 0, B = 0, V = 0, d = 0, CH = 0, nch = 0, S = 1, bf16 = 1;
   const int32_t* root_tok = nullptr;   // [R]
@@ -247,20 +249,27 @@ struct WalkArgs {
   uint8_t* has_child = nullptr;        // [R][B + 1], slot 0 = root
   int32_t* pos = nullptr;              // [R][B + 1] row of the node at its depth
   int32_t* row_req = nullptr;          // [nch * CH]
-  int32_t* row_node = nullptr;         // node index, -1 = root
   int32_t* row_tok = nullptr;
   int32_t* row_src = nullptr;          // residual row (previous depth's rows; s0 row at depth 0)
-  int32_t* ctl = nullptr;              // [1] rows of the current depth
+  int32_t* ctl = nullptr;              // [2] rows of the current depth, inner nodes so far
   int32_t* skip = nullptr;             // [nch] chunk flags
+  int32_t* row_gidx = nullptr;         // [nch * CH] inner-node index of each row
+  int32_t* inner_req = nullptr;        // [nch * CH]
+  int32_t* inner_node = nullptr;       // [nch * CH] node index, -1 = root
+  float* S_inner = nullptr;            // [nch * CH][d] target states of the inner nodes
   const uint64_t* key2 = nullptr;      // merge range results [nch][CH][S] (greedy keys)
   uint16_t* x_hi = nullptr;            // bf16: packed x planes [nch][CH][d]
   uint16_t* x_lo = nullptr;
   float* x_f32 = nullptr;              // fp32: dense x [nch * CH][d]
 };
 hipError_t launch_walk_init(const WalkArgs& a, hipStream_t st);
-// Scatter the target tokens of depth t - 1 (t > 0), then (t < D) compact the
-// rows of depth t and write their x.
+// t < D: compact the rows of depth t, list them as inner nodes and write their
+// x.  t == D: chunk flags of the inner-node list and zero padding rows.
 hipError_t launch_walk_rows(const WalkArgs& a, int t, hipStream_t st);
+// Copy the updated states of the current depth's rows (s_cur, [rows][d]) to
+// their inner-node rows.
+hipError_t launch_walk_keep(const WalkArgs& a, const float* s_cur, hipStream_t st);
+// Target token of every inner node from the head's greedy keys, then the walk.
 hipError_t launch_walk(const WalkArgs& a, hipStream_t st);
 
 // Runs fn(ctx) bracketed by timing events of kernel class cls when kernel

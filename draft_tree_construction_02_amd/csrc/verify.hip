@@ -3,14 +3,16 @@
 // Chain-Trained Corrector to Think in Trees", Core Mechanism, last step; Key
 // Concepts, accepted tokens per verification round).
 //
-// The target is a chain model of the correction head's form.  Its token after
-// a node needs the node's state, which needs the parent's, so the tree is
-// evaluated depth by depth: k_walk_rows lists the nodes of one depth that have
-// children (compacted over all requests), their x = E[tok] + h rows are
-// written as the state update's input, the usual state-update and head
-// kernels run on chunks of those rows (greedy keys only), and the next
-// k_walk_rows call scatters each row's argmax back to its node.  k_walk then
-// follows, per request, the children that match the target.
+// The target is a chain model of the correction head's form.  A node's state
+// needs its parent's, so the states are computed depth by depth: k_walk_rows
+// lists the nodes of one depth that have children (compacted over all
+// requests), their x = E[tok] + h rows are written as the state update's
+// input, the usual state-update kernels run on chunks of those rows, and
+// k_walk_keep files the new states under the nodes' places in one inner-node
+// list.  The target's output head then runs once over that whole list (greedy
+// keys only), so its V x d matrix is streamed once per 128 inner nodes rather
+// than once per depth; k_walk reads each node's argmax and follows, per
+// request, the children that match the target.
 #include "../../include/dartree.h"
 #include "common.hpp"
 #include "launch.hpp"
@@ -48,6 +50,7 @@ __global__ __launch_bounds__(256) void k_walk_init(WalkArgs a) {
   }
   for (int j = threadIdx.x; j < a.D; j += 256) a.path[(long)r * a.D + j] = -1;
   if (threadIdx.x == 0) a.accept_len[r] = 0;
+  if (r == 0 && threadIdx.x == 0) a.ctl[1] = 0;
   __syncthreads();
   const int n = node_count(a, r);
   for (int i = threadIdx.x; i < n; i += 256) {
@@ -56,27 +59,24 @@ __global__ __launch_bounds__(256) void k_walk_init(WalkArgs a) {
   }
 }
 
-// One workgroup.  Scatter depth t - 1's argmax tokens, then list the rows of
-// depth t: the root (t == 0) or the nodes at depth t whose parent has a row
-// at depth t - 1, that have children and a valid token.
+// One workgroup.  t < D: list the rows of depth t - the root (t == 0) or the
+// nodes at depth t whose parent has a row at depth t - 1, that have children
+// and a valid token - and append them to the inner-node list.  t == D: chunk
+// flags of the inner-node list, padding rows of its last chunk zeroed.
 __global__ __launch_bounds__(WALK_THREADS) void k_walk_rows(WalkArgs a, int t) {
   __shared__ int s_wcount[WALK_THREADS / 64];
   __shared__ int s_base;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int B1 = a.B + 1;
-  if (t > 0) {
-    const int nprev = a.ctl[0];
-    for (int m = tid; m < nprev; m += WALK_THREADS) {
-      const uint64_t* kr = a.key2 + (long)m * a.S;   // chunk m / CH, row m % CH
-      uint64_t best = 0;
-      for (int s = 0; s < a.S; ++s) best = kr[s] > best ? kr[s] : best;
-      a.target_tok[(long)a.row_req[m] * B1 + a.row_node[m] + 1] =
-          best != 0 ? (int32_t)key_index(best) : -1;
-    }
+  const int gbase = a.ctl[1];                        // inner nodes listed before depth t
+  if (t >= a.D) {
+    for (int c = tid; c < a.nch; c += WALK_THREADS) a.skip[c] = c * a.CH >= gbase ? 1 : 0;
+    const long lo = (long)gbase * a.d, hi = (long)(gbase + a.CH - 1) / a.CH * a.CH * a.d;
+    for (long i = lo + tid; i < hi; i += WALK_THREADS) a.S_inner[i] = 0.f;
+    return;
   }
-  if (t >= a.D) return;
   if (tid == 0) s_base = 0;
-  __syncthreads();                                   // row lists read before rewritten
+  __syncthreads();
   const long total = (long)a.R * B1;
   for (long g0 = 0; g0 < total; g0 += WALK_THREADS) {
     const long g = g0 + tid;
@@ -115,9 +115,11 @@ __global__ __launch_bounds__(WALK_THREADS) void k_walk_rows(WalkArgs a, int t) {
     if (ok) {
       const int m = base + woff + before;
       a.row_req[m] = r;
-      a.row_node[m] = j - 1;
       a.row_tok[m] = tokv;
       a.row_src[m] = src;
+      a.row_gidx[m] = gbase + m;
+      a.inner_req[gbase + m] = r;
+      a.inner_node[gbase + m] = j - 1;
       a.pos[g] = m;
     }
     __syncthreads();
@@ -129,7 +131,10 @@ __global__ __launch_bounds__(WALK_THREADS) void k_walk_rows(WalkArgs a, int t) {
     __syncthreads();
   }
   const int nt = s_base;
-  if (tid == 0) a.ctl[0] = nt;
+  if (tid == 0) {
+    a.ctl[0] = nt;
+    a.ctl[1] = gbase + nt;
+  }
   for (int c = tid; c < a.nch; c += WALK_THREADS) a.skip[c] = c * a.CH >= nt ? 1 : 0;
   // padding rows of the last non-empty chunk have no residual source
   const int lim = (nt + a.CH - 1) / a.CH * a.CH;
@@ -168,13 +173,35 @@ __global__ __launch_bounds__(WALK_X_THREADS) void k_walk_x(WalkArgs a, int t) {
   }
 }
 
-// One wave per request: from the root, move to the lowest-index child whose
-// token is the target's token after the current node.
-__global__ __launch_bounds__(64) void k_walk(WalkArgs a) {
-  const int r = blockIdx.x, lane = threadIdx.x, B1 = a.B + 1;
+// States of the current depth's rows to their inner-node rows.
+__global__ __launch_bounds__(WALK_X_THREADS) void k_walk_keep(WalkArgs a, const float* s_cur) {
+  const int m = blockIdx.x;
+  if (m >= a.ctl[0]) return;
+  const int k = (blockIdx.y * WALK_X_THREADS + threadIdx.x) * 4;
+  if (k >= a.d) return;
+  *(float4*)(a.S_inner + (long)a.row_gidx[m] * a.d + k) = *(const float4*)(s_cur + (long)m * a.d + k);
+}
+
+// One workgroup per request: the target token of each of the request's inner
+// nodes (the argmax over the head's greedy keys of its row), then one wave
+// moves from the root to the lowest-index child whose token is the target's
+// token after the current node.
+__global__ __launch_bounds__(256) void k_walk(WalkArgs a) {
+  const int r = blockIdx.x, B1 = a.B + 1;
+  int32_t* tt = a.target_tok + (long)r * B1;
+  const int ninner = a.ctl[1];
+  for (int g = threadIdx.x; g < ninner; g += 256) {
+    if (a.inner_req[g] != r) continue;
+    const uint64_t* kr = a.key2 + (long)g * a.S;
+    uint64_t best = 0;
+    for (int s = 0; s < a.S; ++s) best = kr[s] > best ? kr[s] : best;
+    tt[a.inner_node[g] + 1] = best != 0 ? (int32_t)key_index(best) : -1;
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
   const int n = node_count(a, r);
   const long ri = (long)r * a.B;
-  const int32_t* tt = a.target_tok + (long)r * B1;
   int cur = -1, len = 0;
   while (len < a.D) {
     const int want = tt[cur + 1];
@@ -210,8 +237,14 @@ hipError_t launch_walk_rows(const WalkArgs& a, int t, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_walk_keep(const WalkArgs& a, const float* s_cur, hipStream_t st) {
+  const int ny = (a.d + WALK_X_THREADS * 4 - 1) / (WALK_X_THREADS * 4);
+  hipLaunchKernelGGL(k_walk_keep, dim3(a.nch * a.CH, ny), dim3(WALK_X_THREADS), 0, st, a, s_cur);
+  return hipGetLastError();
+}
+
 hipError_t launch_walk(const WalkArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_walk, dim3(a.R), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(k_walk, dim3(a.R), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
