@@ -213,8 +213,13 @@ def main():
     attn_flops = 4.0 * B * (VERIFY["P"] + B) * VERIFY["hd"] * VERIFY["Hq"]
     attn_us = kern["attention"]["avg_us"]
     rows_p = next(m for m in (16, 32, 64, 128) if m >= R * W)   # padded batch rows
-    head_kernel = ("k_head_wide (64 columns per wave, 64/128 rows)"
-                   if wl.wdtype == "bf16" and rows_p >= 64 else "k_head_bf16")
+    if wl.wdtype != "bf16" or rows_p < 64:
+        head_kernel = "k_head_bf16" if wl.wdtype == "bf16" else "k_head_f32"
+    elif rows_p == 64:
+        head_kernel = "k_head_wide (64 columns per wave, 64 rows)"
+    else:
+        head_kernel = "k_head_rows128 (one vocabulary slice per workgroup, 32x32x16 MFMA)"
+
     # weights streamed per step: U (d V) + W1 and W2 (8 d^2) per depth, shared by R requests
     bytes_per_step = D * wbytes * (wl.d * wl.V + 8 * wl.d * wl.d)
     res = {

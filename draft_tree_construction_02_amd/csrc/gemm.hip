@@ -105,6 +105,7 @@ int gemm_gather_max_rows() { return 16 * DT_GATHER_MAX_MT; }
 int gemm_tile_n(int w_bf16) { return w_bf16 ? TN_GEMM : TN_F; }
 int head_tile_n(int w_bf16) { return w_bf16 ? TN_HEAD : TN_F; }
 int head_tiles(const HeadArgs& p) {
+  if (head_rows128_ok(p)) return head_rows128_slices(p);
   const int tn = head_wide_ok(p) ? head_wide_tile_n() : head_tile_n(p.w_bf16);
   return (p.V + tn - 1) / tn;
 }
@@ -766,6 +767,7 @@ static hipError_t head_mt(const HeadArgs& p, hipStream_t st) {
 }
 
 hipError_t launch_head(const HeadArgs& p, hipStream_t st) {
+  if (head_rows128_ok(p)) return launch_head_rows128(p, st);
   if (head_wide_ok(p)) return launch_head_wide(p, st);
   switch (p.Mp) {
     case 16: return head_mt<1>(p, st);

@@ -1,0 +1,283 @@
+// Corrected-logit head for 128 rows (many requests sharing one head), gfx950.
+//
+// Same contract as the other heads (per-row (max, sum exp) and top-k keys of
+// y = s' U / T over each vocabulary slice), shaped for a batch large enough
+// that the matrix cores and the HBM stream have to run at full rate together:
+//   * two workgroups per compute unit, each owning a contiguous slice of
+//     32-column tiles (slices differ by at most one tile), so every unit
+//     streams the same number of bytes and no second round of workgroups
+//     trails behind;
+//   * wave w owns rows 32 w .. 32 w + 31 for all the slice's tiles, so its
+//     accumulators (up to 10 tiles of 32 x 32, all in AGPRs) and its activation
+//     operand (read straight from the packed planes, never shared) are its own,
+//     and the per-row statistics need no exchange between waves;
+//   * the weight tiles of one 32-K step are loaded once per workgroup, each wave
+//     a quarter of them, straight into one of four LDS slots (buffer loads with
+//     the LDS bit) three steps ahead, and all four waves read them from there as
+//     MFMA operands.  Each slot is its own LDS array, so the compiler can tell a
+//     read of one slot from a load into another and never waits for loads
+//     still in flight to later slots; before each barrier a wave waits (an
+//     explicit count) only for its loads into the next step's slot;
+//   * v_mfma_f32_32x32x16_bf16 with the hi/lo activation split.
+// Operand layout (both from 16-row x 32-K packed blocks): lane l takes row
+// 16 ((l % 32) / 16) + l % 16 of a 32-row pair of blocks and, in K step st of
+// the block, K values 16 st + 8 (l / 32) .. + 8, i.e. block lane
+// l % 16 + 16 (2 st + l / 32); the K order inside a step is the same for both
+// operands.  Accumulator element e of lane l is vocabulary column
+// 8 (e / 4) + 4 (l / 32) + e % 4 of the tile and row l % 32 of the wave.
+#include <algorithm>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dt {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int R8_WAVES = 4;                                     // one per 32-row tile
+constexpr int R8_NCMAX = 10;                                    // 32-column tiles per slice at most
+constexpr int R8_AHEAD = 3;                                     // K steps of weights in flight
+constexpr int R8_FPW = (2 * R8_NCMAX + R8_WAVES - 1) / R8_WAVES;  // fragments per wave per step
+constexpr int R8_BLK = 512;                                     // bf16 per 1 KB fragment
+constexpr int R8_SLOT = R8_FPW * R8_WAVES * R8_BLK;             // bf16 per LDS slot (20 KB)
+constexpr int R8_ACT = 4;                                       // activation loads per step
+constexpr int R8_PER_CU = 2;                                    // resident workgroups per unit
+
+int g_cus = 0;
+
+int cu_count() {
+  if (g_cus > 0) return g_cus;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    g_cus = n;
+  return g_cus > 0 ? g_cus : 256;
+}
+
+// Slices of the vocabulary: as many as resident workgroups, each of at most
+// R8_NCMAX tiles and at least 4 (the callers size the partials for slices of
+// 128 columns).
+int r8_slices(int V) {
+  const int nt = (V + 31) / 32;
+  const int need = (nt + R8_NCMAX - 1) / R8_NCMAX;
+  return std::max(std::min((V + 127) / 128, R8_PER_CU * cu_count()), need);
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(64 * R8_WAVES) __attribute__((amdgpu_waves_per_eu(R8_PER_CU, R8_PER_CU)))
+void k_head_rows128(HeadArgs p) {
+  if (p.skip && *p.skip) return;
+  __shared__ __attribute__((aligned(16))) uint16_t Ws0[R8_SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws1[R8_SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws2[R8_SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws3[R8_SLOT];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = gridDim.x, slice = blockIdx.x;
+  const int nt = (p.V + 31) / 32;
+  const int tb = (int)((long)slice * nt / G);
+  const int T = (int)((long)(slice + 1) * nt / G) - tb;         // 1 .. R8_NCMAX
+  const int kblocks = p.d / 32;
+  const int hh = lane >> 5, sub = (lane & 31) >> 4;
+  const int lane_el = sub * R8_BLK + ((lane & 15) + 16 * hh) * 8;
+
+  // weight fragments this wave loads each step: f = wave + 4 i is (tile f / 2,
+  // K step f % 2); fragments past the slice repeat its last tile (in bounds,
+  // loaded to LDS positions that are never read).  Buffer loads: one lane
+  // offset in a VGPR, the fragment's offset in an SGPR; the buffer's size
+  // bounds every access.
+  const int vpad = (p.V + PACK_ROWS - 1) / PACK_ROWS * PACK_ROWS;
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.Ut, (short)0, vpad * p.d * 2, 0x00020000);
+  const int w_lane = lane_el * 2;
+  int wsoff[R8_FPW];
+#pragma unroll
+  for (int i = 0; i < R8_FPW; ++i) {
+    const int f = wave + R8_WAVES * i;
+    const int c = min(f / 2, T - 1), st = f % 2;
+    const int j = tb + c;
+    wsoff[i] = __builtin_amdgcn_readfirstlane(
+        (((j / 4) * kblocks * 8 + 2 * (j % 4)) * R8_BLK + 256 * st) * 2);
+  }
+  // this wave's activation fragments: hi / lo planes, rows 32 wave + ..
+  const __amdgpu_buffer_rsrc_t hrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.pa.hi, (short)0, 128 * p.d * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t lrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.pa.lo, (short)0, 128 * p.d * 2, 0x00020000);
+  const int a_lane = (sub * kblocks * R8_BLK + ((lane & 15) + 16 * hh) * 8) * 2;
+  const int a_wave = __builtin_amdgcn_readfirstlane(2 * wave * kblocks * R8_BLK * 2);
+
+  // R8_FPW loads of step kb's weight fragments into an LDS slot (always issued,
+  // clamped to the last step, so that every step issues the same loads)
+  auto load_w = [&](uint16_t* slot, int kb) {
+    kb = min(kb, kblocks - 1);
+#pragma unroll
+    for (int i = 0; i < R8_FPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wrs, (__attribute__((address_space(3))) void*)(slot + (wave + R8_WAVES * i) * R8_BLK),
+          16, w_lane, wsoff[i] + kb * 8 * R8_BLK * 2, 0, 2 /* nt */);
+  };
+  // R8_ACT loads of step kb's activation fragments into registers
+  u32x4 areg[R8_ACT];                                            // [st * 2 + hl]
+  auto load_a = [&](int kb) {
+    kb = min(kb, kblocks - 1);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int so = a_wave + (kb * R8_BLK + 256 * st) * 2;
+      areg[2 * st] =
+          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hrs, a_lane, so, 0));
+      areg[2 * st + 1] =
+          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(lrs, a_lane, so, 0));
+    }
+  };
+
+  f32x16 acc[R8_NCMAX];
+#pragma unroll
+  for (int c = 0; c < R8_NCMAX; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+
+  // Per step, each wave issues R8_FPW weight loads then R8_ACT activation
+  // loads, and no other vector memory operation.  Before the barrier that ends
+  // step kb a wave needs its loads into step kb + 1's slot to be done (issued
+  // three steps earlier).  The wait below asks for one step more: everything
+  // up to the weight loads of step kb + 2, after which only WAIT_AFTER loads
+  // were issued, so a count that is off by less than a step stays safe.
+  constexpr int WAIT_AFTER = R8_FPW + 2 * R8_ACT;
+  static_assert(WAIT_AFTER < 64, "vmcnt range");
+  constexpr int WAITCNT = (WAIT_AFTER & 15) | ((WAIT_AFTER >> 4) << 14) | (7 << 4) | (15 << 8);
+
+  // prologue: steps 0 .. 2 requested, steps 0 and 1 complete everywhere
+  load_w(Ws0, 0);
+  load_w(Ws1, 1);
+  load_w(Ws2, 2);
+  load_a(0);
+  __builtin_amdgcn_s_waitcnt((R8_ACT + R8_FPW) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // one K step: request step kb + 3 into the slot freed by step kb - 1 and the
+  // activation of step kb + 1, run the MFMAs of step kb from its slot
+  auto step = [&](int kb, uint16_t* cur, uint16_t* ahead) {
+    load_w(ahead, kb + R8_AHEAD);
+    u32x4 acur[R8_ACT];
+#pragma unroll
+    for (int i = 0; i < R8_ACT; ++i) acur[i] = areg[i];
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(kb + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* slot = cur + lane * 8;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const bf16x8 ahi = __builtin_bit_cast(bf16x8, acur[2 * st]);
+      const bf16x8 alo = __builtin_bit_cast(bf16x8, acur[2 * st + 1]);
+#pragma unroll
+      for (int g = 0; g < R8_NCMAX; g += 4) {
+        bf16x8 w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (g + q < R8_NCMAX)
+            w[q] = __builtin_bit_cast(bf16x8,
+                                      *(const u32x4*)(slot + (2 * (g + q) + st) * R8_BLK));
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (g + q < R8_NCMAX)
+            acc[g + q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[q], ahi, acc[g + q], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (g + q < R8_NCMAX)
+            acc[g + q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[q], alo, acc[g + q], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(WAITCNT);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // kblocks % 4 == 0: slot of step kb is kb % 4, static in the unrolled body
+  for (int kb = 0; kb < kblocks; kb += 4) {
+    step(kb, Ws0, Ws3);
+    step(kb + 1, Ws1, Ws0);
+    step(kb + 2, Ws2, Ws1);
+    step(kb + 3, Ws3, Ws2);
+  }
+  // loads past the last step may still be landing in LDS: let them finish
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+
+  // per-row statistics of the slice: lanes l and l ^ 32 hold the same row
+  const float scale = p.greedy ? 1.f : p.inv_T;
+  const int col0 = 32 * tb + 4 * hh;
+  float mx = -INFINITY;
+  TopK<KMAX> tk;
+  tk.clear();
+#pragma unroll
+  for (int c = 0; c < R8_NCMAX; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int col = col0 + 32 * c + 8 * (e >> 2) + (e & 3);
+      const float v = acc[c][e] * scale;
+      if (c < T && col < p.V) {
+        mx = fmaxf(mx, v);
+        tk.insert(make_key(v, (uint32_t)col));
+      }
+    }
+  float sum = 0.f;
+  if (!p.greedy) {
+#pragma unroll
+    for (int c = 0; c < R8_NCMAX; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int col = col0 + 32 * c + 8 * (e >> 2) + (e & 3);
+        if (c < T && col < p.V) sum += expf(acc[c][e] * scale - mx);
+      }
+  }
+  MaxSum ms{mx, sum};
+  {
+    const float m2 = __shfl_xor(ms.m, 32, WAVE);
+    const float s2 = __shfl_xor(ms.s, 32, WAVE);
+    ms.combine(m2, s2);
+    uint64_t o[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) o[i] = shfl_xor_u64(tk.v[i], 32);
+    tk.merge(o);
+  }
+  if (lane < 32) {
+    const long o = (long)(32 * wave + lane) * G + slice;
+    p.ms_part[o] = make_float2(ms.m, ms.s);
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i)
+      if (i < p.k) p.key_part[o * p.k + i] = tk.v[i];
+  }
+}
+
+}  // namespace
+
+#ifndef DT_ROWS128
+#define DT_ROWS128 1
+#endif
+
+bool head_rows128_ok(const HeadArgs& p) {
+  const long vpad = (long)(p.V + PACK_ROWS - 1) / PACK_ROWS * PACK_ROWS;
+  return DT_ROWS128 && p.w_bf16 && p.w_packed && p.Mp == 128 && p.d % 128 == 0 &&
+         vpad * p.d * 2 < (1L << 31);
+}
+
+int head_rows128_slices(const HeadArgs& p) { return r8_slices(p.V); }
+
+hipError_t launch_head_rows128(const HeadArgs& p, hipStream_t st) {
+  const dim3 grid(r8_slices(p.V));
+  switch (p.kmax) {
+    case 1: hipLaunchKernelGGL(k_head_rows128<1>, grid, dim3(64 * R8_WAVES), 0, st, p); break;
+    case 4: hipLaunchKernelGGL(k_head_rows128<4>, grid, dim3(64 * R8_WAVES), 0, st, p); break;
+    case 8: hipLaunchKernelGGL(k_head_rows128<8>, grid, dim3(64 * R8_WAVES), 0, st, p); break;
+    case 16: hipLaunchKernelGGL(k_head_rows128<16>, grid, dim3(64 * R8_WAVES), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dt

@@ -105,6 +105,11 @@ hipError_t launch_head(const HeadArgs& h, hipStream_t st);
 bool head_wide_ok(const HeadArgs& h);
 int head_wide_tile_n();
 hipError_t launch_head_wide(const HeadArgs& h, hipStream_t st);
+// 128-row packed bf16 variant (head_rows128.hip): one vocabulary slice per
+// compute unit; launch_head prefers it over the 64/128-row one
+bool head_rows128_ok(const HeadArgs& h);
+int head_rows128_slices(const HeadArgs& h);
+hipError_t launch_head_rows128(const HeadArgs& h, hipStream_t st);
 
 // Per-row merge of the head's tile partials (kt keys per tile): log-sum-exp
 // and global top-k, written to cand_tok / cand_lp rows of stride k.  ms2 and
