@@ -45,15 +45,19 @@ constexpr int R8_SLOT = R8_FPW * R8_WAVES * R8_BLK;             // bf16 per LDS 
 constexpr int R8_ACT = 4;                                       // activation loads per step
 constexpr int R8_PER_CU = 2;                                    // resident workgroups per unit
 
-int g_cus = 0;
+// Compute units of the current device, queried once per device (a stale
+// read by a concurrent first caller only repeats the query).
+constexpr int R8_MAX_DEVICES = 64;
+int g_cus[R8_MAX_DEVICES] = {};
 
 int cu_count() {
-  if (g_cus > 0) return g_cus;
   int dev = 0, n = 0;
-  if (hipGetDevice(&dev) == hipSuccess &&
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-    g_cus = n;
-  return g_cus > 0 ? g_cus : 256;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < R8_MAX_DEVICES && g_cus[dev] > 0) return g_cus[dev];
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  if (dev < R8_MAX_DEVICES) g_cus[dev] = n;
+  return n;
 }
 
 // Slices of the vocabulary: as many as resident workgroups, each of at most

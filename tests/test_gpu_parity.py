@@ -130,6 +130,11 @@ def test_build_is_deterministic():
     ("bf16_T1", 20, 8, 1.0, False), ("bf16_T1", 20, 8, 1.0, True),
     ("bf16_T1", 16, 4, 0.5, True), ("bf16_T1", 33, 16, 2.0, True),
     ("bf16_T1", 128, 8, 1.0, True), ("bf16_T1", 64, 1, 1.0, True),
+    # the 128-row kernel: 16 keys, d = 128 (one unrolled group of K steps),
+    # a ragged vocabulary tile (V = 3001) at d = 384, greedy, and more rows
+    # than fill 128 (padding rows)
+    ("bf16_k16", 128, 16, 1.3, True), ("bf16_ragged_rows", 128, 3, 0.7, True),
+    ("bf16_T0", 128, 4, 0.0, True), ("bf16_T1", 100, 4, 1.0, True),
     ("bf16_T0", 7, 8, 0.0, True), ("bf16_ragged_rows", 50, 3, 0.7, False),
     ("tiny", 4, 4, 1.0, False), ("f32_wide", 70, 5, 1.0, False)])
 def test_corrected_topk_matches_oracle(name, rows, k, T, packed):
