@@ -62,13 +62,11 @@ namespace dt {
 #ifndef DT_PRIO
 #define DT_PRIO 1
 #endif
-// 1: each wave reads its activation blocks straight from L2 (no LDS staging,
-// no barrier in the K loop); 0: the workgroup stages them once in LDS.
+// 1: a K iteration requests its activation chunk before its weight
+// fragments, so the wait before the LDS store of the activation does not also
+// wait for the weights (vector memory counters complete in order); 0: after.
 #ifndef DT_AFIRST
 #define DT_AFIRST 1
-#endif
-#ifndef DT_DIRECT_A
-#define DT_DIRECT_A 0
 #endif
 
 constexpr int NT = 256;               // threads per workgroup (fp32 path, helpers)
@@ -80,20 +78,6 @@ constexpr int KC_F = 32;              // K staged per LDS chunk (fp32 path)
 constexpr int CPAD = 4;               // C tile row padding (floats)
 constexpr int BLK = 512;              // bf16 elements per packed block (1 KB)
 
-#ifdef DT_TRACE
-// per-workgroup timestamps of the bf16 mainloop (experimental builds only)
-__device__ unsigned long long g_trace[4 * 16384];
-__device__ __forceinline__ void trace_mark(int slot) {
-  const int wg = blockIdx.x + gridDim.x * blockIdx.y;
-  if (threadIdx.x == 0 && wg < 16384) g_trace[4 * wg + slot] = __builtin_amdgcn_s_memrealtime();
-}
-extern "C" int dt_trace_read(void* host, size_t bytes) {
-  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_trace), bytes) == hipSuccess ? 0 : -4;
-}
-#define DT_MARK(s) trace_mark(s)
-#else
-#define DT_MARK(s)
-#endif
 
 // bf16: largest row-tile count whose first product forms x while staging
 // (beyond it a separate kernel writes the x planes first)
@@ -331,46 +315,12 @@ __device__ __forceinline__ void tile_bf16(const ASource& a, const uint16_t* __re
       }
       __syncthreads();
     }
-  } else if constexpr (DT_DIRECT_A != 0) {
-    // activation fragments straight from the packed planes in L2
-    const int kblocks = a.K / 32;
-    for (int s = 0; s < klen / 128; ++s) {
-      const int k = k0 + s * 128;
-      u32x4 b[NW][4], ah[MT][4], al[MT][4];
-      load_b<NW, PW>(b, Wt, a.K, col0, N, k, lane);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const long off = ((long)mt * kblocks + k / 32 + j) * BLK + lane * 8;
-          ah[mt][j] = *(const u32x4*)(a.hi + off);
-          al[mt][j] = *(const u32x4*)(a.lo + off);
-        }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-          for (int c = 0; c < NW; ++c)
-            acc[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, b[c][j]), __builtin_bit_cast(bf16x8, ah[mt][j]),
-                acc[c][mt], 0, 0, 0);
-#pragma unroll
-          for (int c = 0; c < NW; ++c)
-            acc[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, b[c][j]), __builtin_bit_cast(bf16x8, al[mt][j]),
-                acc[c][mt], 0, 0, 0);
-        }
-    }
-    __syncthreads();
   } else {
     // no register prefetch: weights and the activation chunk of iteration s
     // are requested together; other resident waves cover the latency
-    DT_MARK(0);
     if (DT_PRIO != 0) __builtin_amdgcn_s_setprio(3);
     for (int s = 0; s < nst; ++s) {
       const int k = k0 + s * C::KC;
-      if (s == 1) DT_MARK(1);
       if (DT_PRIO == 1) {
         const int pr = 3 - (4 * s) / nst;
         if (pr == 2) __builtin_amdgcn_s_setprio(2);
@@ -392,7 +342,6 @@ __device__ __forceinline__ void tile_bf16(const ASource& a, const uint16_t* __re
       for (int it = 0; it < IPS; ++it) mma_iter<MT, C::KC, NW>(Ab, it, b[it], acc, lane);
     }
     __syncthreads();
-    DT_MARK(2);
   }
 }
 
@@ -524,7 +473,6 @@ __global__ __launch_bounds__(64 * DT_WV_GEMM) void k_gemm_bf16(GemmArgs g) {
       *(float4*)(g.part + ((long)split * Mp + m) * g.N + n) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
-  DT_MARK(3);
 }
 
 template <int MT, bool GATHER>
@@ -677,7 +625,6 @@ __attribute__((amdgpu_waves_per_eu(DT_HEAD_WPE, 8))) void k_head_bf16(HeadArgs p
     }
   __syncthreads();
   head_epilogue<MT, KMAX, TN, 64 * DT_WV_HEAD>(p, Cs, tile);
-  DT_MARK(3);
 }
 
 template <int MT, int KMAX>
