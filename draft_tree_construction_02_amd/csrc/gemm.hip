@@ -677,6 +677,7 @@ static hipError_t gemm_mt(const GemmArgs& g, hipStream_t st) {
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
+  if (gemm_rows128_ok(g)) return launch_gemm_rows128(g, st);
   switch (g.Mp) {
     case 16: return gemm_mt<1>(g, st);
     case 32: return gemm_mt<2>(g, st);

@@ -39,9 +39,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 constexpr int R8_WAVES = 4;                                     // one per 32-row tile
 constexpr int R8_NCMAX = 10;                                    // 32-column tiles per slice at most
 constexpr int R8_AHEAD = 3;                                     // K steps of weights in flight
-constexpr int R8_FPW = (2 * R8_NCMAX + R8_WAVES - 1) / R8_WAVES;  // fragments per wave per step
 constexpr int R8_BLK = 512;                                     // bf16 per 1 KB fragment
-constexpr int R8_SLOT = R8_FPW * R8_WAVES * R8_BLK;             // bf16 per LDS slot (20 KB)
 constexpr int R8_ACT = 4;                                       // activation loads per step
 constexpr int R8_PER_CU = 2;                                    // resident workgroups per unit
 
@@ -69,36 +67,46 @@ int r8_slices(int V) {
   return std::max(std::min((V + 127) / 128, R8_PER_CU * cu_count()), need);
 }
 
-template <int KMAX>
-__global__ __launch_bounds__(64 * R8_WAVES) __attribute__((amdgpu_waves_per_eu(R8_PER_CU, R8_PER_CU)))
-void k_head_rows128(HeadArgs p) {
-  if (p.skip && *p.skip) return;
-  __shared__ __attribute__((aligned(16))) uint16_t Ws0[R8_SLOT];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws1[R8_SLOT];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws2[R8_SLOT];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws3[R8_SLOT];
+// Fragments per wave per K step and bf16 per LDS slot for NC tiles of 32
+// columns per workgroup.
+template <int NC>
+struct R8Cfg {
+  static constexpr int FPW = (2 * NC + R8_WAVES - 1) / R8_WAVES;
+  static constexpr int SLOT = FPW * R8_WAVES * R8_BLK;
+};
+
+// The K loop shared by the 128-row head and the 128-row GEMM: wave w
+// accumulates rows 32 w .. 32 w + 31 of Y = A W^T for the workgroup's tiles
+// tb .. tb + T - 1 (T <= NC; 32 columns each) over K blocks kb0 .. kb0 + nkb
+// - 1 (32 K each, nkb % 4 == 0).  W is a packed bf16 matrix (grouped layout)
+// of nrows_pad rows and K columns; A the packed hi/lo planes of 128 rows.
+// Ws0..Ws3 are the workgroup's four LDS slots (distinct arrays).  TAG makes
+// the instantiation (and its lambdas) distinct per kernel: host stubs of
+// kernels that share one instantiation are not all emitted.
+template <int NC, int TAG>
+__device__ __forceinline__ void r8_mainloop(const uint16_t* W, int nrows_pad, int K,
+                                            const PackedA& pa, int tb, int T, int kb0, int nkb,
+                                            f32x16 (&acc)[NC], uint16_t* Ws0, uint16_t* Ws1,
+                                            uint16_t* Ws2, uint16_t* Ws3) {
+  using C = R8Cfg<NC>;
+  constexpr int FPW = C::FPW;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int G = gridDim.x, slice = blockIdx.x;
-  const int nt = (p.V + 31) / 32;
-  const int tb = (int)((long)slice * nt / G);
-  const int T = (int)((long)(slice + 1) * nt / G) - tb;         // 1 .. R8_NCMAX
-  const int kblocks = p.d / 32;
+  const int kblocks = K / 32, kb_last = kb0 + nkb - 1;
   const int hh = lane >> 5, sub = (lane & 31) >> 4;
   const int lane_el = sub * R8_BLK + ((lane & 15) + 16 * hh) * 8;
 
   // weight fragments this wave loads each step: f = wave + 4 i is (tile f / 2,
-  // K step f % 2); fragments past the slice repeat its last tile (in bounds,
-  // loaded to LDS positions that are never read).  Buffer loads: one lane
-  // offset in a VGPR, the fragment's offset in an SGPR; the buffer's size
-  // bounds every access.
-  const int vpad = (p.V + PACK_ROWS - 1) / PACK_ROWS * PACK_ROWS;
+  // K step f % 2); fragments past the workgroup's tiles repeat its last tile
+  // (in bounds, loaded to LDS positions that are never read).  Buffer loads:
+  // one lane offset in a VGPR, the fragment's offset in an SGPR; the buffer's
+  // size bounds every access.
   const __amdgpu_buffer_rsrc_t wrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.Ut, (short)0, vpad * p.d * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, nrows_pad * K * 2, 0x00020000);
   const int w_lane = lane_el * 2;
-  int wsoff[R8_FPW];
+  int wsoff[FPW];
 #pragma unroll
-  for (int i = 0; i < R8_FPW; ++i) {
+  for (int i = 0; i < FPW; ++i) {
     const int f = wave + R8_WAVES * i;
     const int c = min(f / 2, T - 1), st = f % 2;
     const int j = tb + c;
@@ -107,18 +115,18 @@ void k_head_rows128(HeadArgs p) {
   }
   // this wave's activation fragments: hi / lo planes, rows 32 wave + ..
   const __amdgpu_buffer_rsrc_t hrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.pa.hi, (short)0, 128 * p.d * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)pa.hi, (short)0, 128 * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t lrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.pa.lo, (short)0, 128 * p.d * 2, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)pa.lo, (short)0, 128 * K * 2, 0x00020000);
   const int a_lane = (sub * kblocks * R8_BLK + ((lane & 15) + 16 * hh) * 8) * 2;
   const int a_wave = __builtin_amdgcn_readfirstlane(2 * wave * kblocks * R8_BLK * 2);
 
-  // R8_FPW loads of step kb's weight fragments into an LDS slot (always issued,
+  // FPW loads of step kb's weight fragments into an LDS slot (always issued,
   // clamped to the last step, so that every step issues the same loads)
   auto load_w = [&](uint16_t* slot, int kb) {
-    kb = min(kb, kblocks - 1);
+    kb = min(kb, kb_last);
 #pragma unroll
-    for (int i = 0; i < R8_FPW; ++i)
+    for (int i = 0; i < FPW; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wrs, (__attribute__((address_space(3))) void*)(slot + (wave + R8_WAVES * i) * R8_BLK),
           16, w_lane, wsoff[i] + kb * 8 * R8_BLK * 2, 0, 2 /* nt */);
@@ -126,7 +134,7 @@ void k_head_rows128(HeadArgs p) {
   // R8_ACT loads of step kb's activation fragments into registers
   u32x4 areg[R8_ACT];                                            // [st * 2 + hl]
   auto load_a = [&](int kb) {
-    kb = min(kb, kblocks - 1);
+    kb = min(kb, kb_last);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int so = a_wave + (kb * R8_BLK + 256 * st) * 2;
@@ -137,28 +145,27 @@ void k_head_rows128(HeadArgs p) {
     }
   };
 
-  f32x16 acc[R8_NCMAX];
 #pragma unroll
-  for (int c = 0; c < R8_NCMAX; ++c)
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
 
-  // Per step, each wave issues R8_FPW weight loads then R8_ACT activation
-  // loads, and no other vector memory operation.  Before the barrier that ends
-  // step kb a wave needs its loads into step kb + 1's slot to be done (issued
-  // three steps earlier).  The wait below asks for one step more: everything
-  // up to the weight loads of step kb + 2, after which only WAIT_AFTER loads
-  // were issued, so a count that is off by less than a step stays safe.
-  constexpr int WAIT_AFTER = R8_FPW + 2 * R8_ACT;
+  // Per step, each wave issues FPW weight loads then R8_ACT activation loads,
+  // and no other vector memory operation.  Before the barrier that ends step
+  // kb a wave needs its loads into step kb + 1's slot to be done (issued three
+  // steps earlier).  The wait below asks for one step more: everything up to
+  // the weight loads of step kb + 2, after which only WAIT_AFTER loads were
+  // issued, so a count that is off by less than a step stays safe.
+  constexpr int WAIT_AFTER = FPW + 2 * R8_ACT;
   static_assert(WAIT_AFTER < 64, "vmcnt range");
   constexpr int WAITCNT = (WAIT_AFTER & 15) | ((WAIT_AFTER >> 4) << 14) | (7 << 4) | (15 << 8);
 
   // prologue: steps 0 .. 2 requested, steps 0 and 1 complete everywhere
-  load_w(Ws0, 0);
-  load_w(Ws1, 1);
-  load_w(Ws2, 2);
-  load_a(0);
-  __builtin_amdgcn_s_waitcnt((R8_ACT + R8_FPW) | (7 << 4) | (15 << 8));
+  load_w(Ws0, kb0);
+  load_w(Ws1, kb0 + 1);
+  load_w(Ws2, kb0 + 2);
+  load_a(kb0);
+  __builtin_amdgcn_s_waitcnt((R8_ACT + FPW) | (7 << 4) | (15 << 8));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -179,20 +186,20 @@ void k_head_rows128(HeadArgs p) {
       const bf16x8 ahi = __builtin_bit_cast(bf16x8, acur[2 * st]);
       const bf16x8 alo = __builtin_bit_cast(bf16x8, acur[2 * st + 1]);
 #pragma unroll
-      for (int g = 0; g < R8_NCMAX; g += 4) {
+      for (int g = 0; g < NC; g += 4) {
         bf16x8 w[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (g + q < R8_NCMAX)
+          if (g + q < NC)
             w[q] = __builtin_bit_cast(bf16x8,
                                       *(const u32x4*)(slot + (2 * (g + q) + st) * R8_BLK));
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (g + q < R8_NCMAX)
+          if (g + q < NC)
             acc[g + q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[q], ahi, acc[g + q], 0, 0, 0);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (g + q < R8_NCMAX)
+          if (g + q < NC)
             acc[g + q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[q], alo, acc[g + q], 0, 0, 0);
       }
     }
@@ -202,8 +209,8 @@ void k_head_rows128(HeadArgs p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // kblocks % 4 == 0: slot of step kb is kb % 4, static in the unrolled body
-  for (int kb = 0; kb < kblocks; kb += 4) {
+  // nkb % 4 == 0: the slot of step kb0 + i is i % 4, static in the unrolled body
+  for (int kb = kb0; kb <= kb_last; kb += 4) {
     step(kb, Ws0, Ws3);
     step(kb + 1, Ws1, Ws0);
     step(kb + 2, Ws2, Ws1);
@@ -211,6 +218,28 @@ void k_head_rows128(HeadArgs p) {
   }
   // loads past the last step may still be landing in LDS: let them finish
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(64 * R8_WAVES) __attribute__((amdgpu_waves_per_eu(R8_PER_CU, R8_PER_CU)))
+void k_head_rows128(HeadArgs p) {
+  if (p.skip && *p.skip) return;
+  using C = R8Cfg<R8_NCMAX>;
+  __shared__ __attribute__((aligned(16))) uint16_t Ws0[C::SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws1[C::SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws2[C::SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws3[C::SLOT];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = gridDim.x, slice = blockIdx.x;
+  const int nt = (p.V + 31) / 32;
+  const int tb = (int)((long)slice * nt / G);
+  const int T = (int)((long)(slice + 1) * nt / G) - tb;         // 1 .. R8_NCMAX
+  const int hh = lane >> 5;
+  const int vpad = (p.V + PACK_ROWS - 1) / PACK_ROWS * PACK_ROWS;
+  f32x16 acc[R8_NCMAX];
+  r8_mainloop<R8_NCMAX, KMAX>((const uint16_t*)p.Ut, vpad, p.d, p.pa, tb, T, 0, p.d / 32, acc,
+                              Ws0, Ws1, Ws2, Ws3);
 
   // per-row statistics of the slice: lanes l and l ^ 32 hold the same row
   const float scale = p.greedy ? 1.f : p.inv_T;
@@ -258,6 +287,44 @@ void k_head_rows128(HeadArgs p) {
   }
 }
 
+// Split-K partial products of a 128-row GEMM on the same K loop: workgroup
+// (slice, split) owns R8_GEMM_NC tiles of 32 output columns and K blocks
+// [split * nkb, (split + 1) * nkb); wave w writes rows 32 w .. + 31 of
+// part[split][128][N] (fp32), which the split-K reduction then sums in order.
+constexpr int R8_GEMM_NC = 4;
+
+__global__ __launch_bounds__(64 * R8_WAVES) __attribute__((amdgpu_waves_per_eu(2)))
+void k_gemm_rows128(GemmArgs g) {
+  if (g.skip && *g.skip) return;
+  using C = R8Cfg<R8_GEMM_NC>;
+  __shared__ __attribute__((aligned(16))) uint16_t Ws0[C::SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws1[C::SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws2[C::SLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws3[C::SLOT];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slice = blockIdx.x, split = blockIdx.y;
+  const int nt = g.N / 32;
+  const int tb = slice * R8_GEMM_NC;
+  const int T = min(R8_GEMM_NC, nt - tb);
+  const int nkb = g.K / 32 / g.splits;
+  const int npad = (g.N + PACK_ROWS - 1) / PACK_ROWS * PACK_ROWS;
+  f32x16 acc[R8_GEMM_NC];
+  r8_mainloop<R8_GEMM_NC, 0>((const uint16_t*)g.Wt, npad, g.K, g.pa, tb, T, split * nkb, nkb,
+                             acc, Ws0, Ws1, Ws2, Ws3);
+  // element e of lane l in tile c: row l % 32 of the wave, column
+  // 32 (tb + c) + 8 (e / 4) + 4 (l / 32) + e % 4
+  const int row = 32 * wave + (lane & 31);
+  float* out = g.part + ((long)split * 128 + row) * g.N + 4 * (lane >> 5);
+#pragma unroll
+  for (int c = 0; c < R8_GEMM_NC; ++c)
+    if (c < T)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(f32x4*)(out + 32 * (tb + c) + 8 * q) =
+            f32x4{acc[c][4 * q], acc[c][4 * q + 1], acc[c][4 * q + 2], acc[c][4 * q + 3]};
+}
+
 }  // namespace
 
 #ifndef DT_ROWS128
@@ -271,6 +338,20 @@ bool head_rows128_ok(const HeadArgs& p) {
 }
 
 int head_rows128_slices(const HeadArgs& p) { return r8_slices(p.V); }
+
+bool gemm_rows128_ok(const GemmArgs& g) {
+  const long npad = (long)(g.N + PACK_ROWS - 1) / PACK_ROWS * PACK_ROWS;
+  const int kblocks = g.K / 32;
+  return DT_ROWS128 && g.w_bf16 && g.w_packed && g.Mp == 128 && g.N % 32 == 0 &&
+         g.K % 32 == 0 && g.splits >= 1 && kblocks % g.splits == 0 &&
+         (kblocks / g.splits) % 4 == 0 && npad * g.K * 2 < (1L << 31);
+}
+
+hipError_t launch_gemm_rows128(const GemmArgs& g, hipStream_t st) {
+  const dim3 grid((g.N / 32 + R8_GEMM_NC - 1) / R8_GEMM_NC, g.splits);
+  hipLaunchKernelGGL(k_gemm_rows128, grid, dim3(64 * R8_WAVES), 0, st, g);
+  return hipGetLastError();
+}
 
 hipError_t launch_head_rows128(const HeadArgs& p, hipStream_t st) {
   const dim3 grid(r8_slices(p.V));

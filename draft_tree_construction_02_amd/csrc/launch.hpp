@@ -110,6 +110,9 @@ hipError_t launch_head_wide(const HeadArgs& h, hipStream_t st);
 bool head_rows128_ok(const HeadArgs& h);
 int head_rows128_slices(const HeadArgs& h);
 hipError_t launch_head_rows128(const HeadArgs& h, hipStream_t st);
+// 128-row packed bf16 GEMM on the same K loop (split-K partials as launch_gemm)
+bool gemm_rows128_ok(const GemmArgs& g);
+hipError_t launch_gemm_rows128(const GemmArgs& g, hipStream_t st);
 
 // Per-row merge of the head's tile partials (kt keys per tile): log-sum-exp
 // and global top-k, written to cand_tok / cand_lp rows of stride k.  ms2 and

@@ -175,7 +175,10 @@ def test_corrected_topk_matches_oracle(name, rows, k, T, packed):
 @pytest.mark.parametrize("name,rows,packed", [("bf16_T1", 20, False), ("bf16_T1", 20, True),
                                               ("bf16_ragged_rows", 18, True),
                                               ("bf16_ragged_rows", 100, False), ("tiny", 4, False),
-                                              ("f32_wide", 80, False)])
+                                              ("f32_wide", 80, False),
+                                              # the 128-row GEMM (packed, 65..128 rows)
+                                              ("bf16_ragged_rows", 100, True),
+                                              ("bf16_T1", 128, True), ("bf16_k16", 77, True)])
 def test_state_update_matches_oracle(name, rows, packed):
     wl = small_cases()[name]
     hw, _, head, ohead = case_inputs(wl, packed)
