@@ -72,6 +72,8 @@ def parse():
                     help="skip the sequential best-first (one head call per node) comparison")
     ap.add_argument("--no-walk", action="store_true",
                     help="skip the acceptance walk against the synthetic target")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the timing of the step captured in a HIP graph")
     ap.add_argument("--cpu-builds", type=int, default=1,
                     help="oracle builds timed for cpu_baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -208,6 +210,31 @@ def main():
     log(f"[bench] head kernel {head_us:.1f} us/launch -> {achieved:.0f} GB/s; "
         f"per-kernel timed region {pk_ms / args.steps:.3f} ms/step")
 
+    # hipGraph on/off: the same step captured once and replayed
+    graph_res = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        g_ms, g_wall, g_per = timed_region(graph.replay, False)
+        g_step = max(g_ms, g_wall * 1e3) / args.steps
+        graph_res = {"ms_per_step": round(g_step, 4), "builds_per_s": round(R * 1e3 / g_step, 3),
+                     "median_ms": round(pct(g_per, 0.5), 4)}
+        log(f"[bench] step replayed from a HIP graph: {g_step:.3f} ms/step "
+            f"(eager {ms_per_step:.3f})")
+        del graph
+    probe = hbm_probe(A, torch, dev)
+    log(f"[bench] read probe: {probe['bytes'] / 2 ** 30:.0f} GiB in {probe['us']:.1f} us "
+        f"-> {probe['gbs']:.0f} GB/s")
+
     builds_per_s = R * 1e3 / ms_per_step
     # verification layer: QK^T and PV over prefix + tree keys for every query head
     attn_flops = 4.0 * B * (VERIFY["P"] + B) * VERIFY["hd"] * VERIFY["Hq"]
@@ -242,7 +269,11 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": profiled_traffic(wl.name),
                      "kernel": f"corrected-logit head ({head_kernel})",
-                     "bytes_per_launch": head_bytes},
+                     "bytes_per_launch": head_bytes,
+                     "probe_gbs": probe["gbs"],
+                     "frac_of_probe": round(achieved / probe["gbs"], 4)},
+        "hbm_probe": probe,
+        "graph": graph_res,
         "step_ms": {"mean": round(ms_per_step, 4), "median": round(pct(per, 0.5), 4),
                     "p10": round(pct(per, 0.1), 4), "p90": round(pct(per, 0.9), 4)},
         "builds_per_s_build_only": round(R * 1e3 * args.steps / max(b_ms, b_wall * 1e3), 3),
@@ -267,6 +298,31 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, hw, req, args.cpu_builds)
     print(json.dumps(res), flush=True)
+
+
+def hbm_probe(A, torch, dev, nbytes=2 << 30, reps=10):
+    """Practical read bandwidth: the library's streaming read probe over a
+    2 GiB buffer, averaged over `reps` calls timed with events on the stream it
+    runs on (each call is a one-thread clear kernel plus the read)."""
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    out = torch.empty(1, dtype=torch.int64, device=dev)
+    for _ in range(2):
+        A.hbm_read_probe(buf, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        A.hbm_read_probe(buf, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    # every 64-bit word holds two int32 ones: 2^32 + 1
+    got = int(out.cpu().numpy().view("uint64")[0])
+    if got != (nbytes // 8) * (2 ** 32 + 1) % 2 ** 64:
+        raise RuntimeError("read probe returned a wrong sum")
+    del buf
+    torch.cuda.empty_cache()
+    return {"bytes": nbytes, "us": round(us, 2), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
 def sequential_baseline(A, head, h, s0, root, wl, b_ms, b_wall, bpm_ms, bpm_wall, steps):

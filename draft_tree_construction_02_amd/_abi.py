@@ -30,7 +30,7 @@ EXPORTS = [
     "build_tree_sequential_workspace_size", "build_tree_sequential",
     "prune_topB", "build_tree_mask",
     "tree_attention_workspace_size", "tree_attention_verify",
-    "accept_walk_workspace_size", "accept_walk",
+    "accept_walk_workspace_size", "accept_walk", "hbm_read_probe",
     "dartree_timing_enable", "dartree_timing_reset", "dartree_timing_read",
 ]
 
@@ -93,6 +93,7 @@ def lib():
             "accept_walk_workspace_size": (sz, [hp, i32, i32, i32]),
             "accept_walk": (i32, [hp, vp, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp,
                                   vp, vp, vp, vp, sz, vp]),
+            "hbm_read_probe": (i32, [vp, sz, vp, vp]),
             "dartree_timing_enable": (i32, [i32]),
             "dartree_timing_reset": (i32, []),
             "dartree_timing_read": (i32, [i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
@@ -395,6 +396,23 @@ def accept_walk(target: Head, h, s0, root_tok, tok, parent, depth, n, tok_index=
                            _ptr(n), _ptr(out["target_tok"]), _ptr(out["path"]),
                            _ptr(out["accept_len"]), _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "accept_walk")
+    return out
+
+
+def hbm_read_probe(buf, out=None, stream=None):
+    """Sum of the 64-bit words of a contiguous device tensor (mod 2^64), read
+    once by the streaming probe; returns a device int64 tensor of one element
+    (the sum's bits)."""
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda":
+        raise ValueError("buf must be a device tensor")
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty(1, dtype=torch.int64, device=buf.device)
+    _dev(out, torch.int64, "out", (1,))
+    rc = lib().hbm_read_probe(_ptr(buf) if nbytes else None, nbytes, _ptr(out), _stream(stream))
+    _check(rc, "hbm_read_probe")
     return out
 
 

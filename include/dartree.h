@@ -384,6 +384,25 @@ int accept_walk(const dt_head* target, const float* h, const float* s0,
                 size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Read-bandwidth probe                                                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * hbm_read_probe - reads every byte of a device buffer once (a plain
+ * streaming read by a grid of resident workgroups) and writes the sum of its
+ * little-endian 64-bit words modulo 2^64 to *sum (device memory).  Timed over
+ * a buffer of a few GB it gives the practical device-memory read bandwidth
+ * against which the head's weight stream (2 d V bytes per depth, [P3]
+ * Summary & Methodology Analysis: drafting is memory-bandwidth bound) is
+ * reported; the sum makes the read checkable and keeps it from being elided.
+ *   buf   device pointer, 16-byte aligned (may be NULL when bytes == 0)
+ *   bytes multiple of 8; 0 gives *sum = 0
+ *   sum   device uint64_t[1], written on `stream`
+ * Two launches (clear, read); no workspace.
+ */
+int hbm_read_probe(const void* buf, size_t bytes, uint64_t* sum, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Kernel timing (off by default)                                            */
 /* ------------------------------------------------------------------------ */
 

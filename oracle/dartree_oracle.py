@@ -497,3 +497,22 @@ def tree_attention(q, k_prefix, v_prefix, k_tree, v_tree, mask, n: int, scale: f
         p /= np.sum(p, axis=1, keepdims=True)
         out[:, h] = p @ np.concatenate([vp[:, g], vt[:n, g]], axis=0)
     return out
+
+
+# ----------------------------------------------------------------------------
+# measurement: checksum of the read-bandwidth probe
+# ----------------------------------------------------------------------------
+def word_sum64(buf) -> int:
+    """Sum of the little-endian unsigned 64-bit words of a byte buffer, modulo
+    2^64: what the streaming read probe returns for the buffer it reads (the
+    probe sets the ceiling for the memory-bound weight stream of "Accelerating
+    Language Models with Diffusion Draft Trees", Summary & Methodology
+    Analysis).  ``buf`` is bytes or a numpy array; its size must be a
+    multiple of 8."""
+    raw = np.frombuffer(buf, np.uint8) if isinstance(buf, (bytes, bytearray)) else \
+        np.ascontiguousarray(buf).reshape(-1).view(np.uint8)
+    if raw.size % 8:
+        raise ValueError("buffer size must be a multiple of 8 bytes")
+    words = raw.view("<u8")
+    # numpy's unsigned integer sums wrap modulo 2^64
+    return int(np.sum(words, dtype=np.uint64)) if words.size else 0

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     L = A.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -240,3 +240,12 @@ def test_timing_api_without_launches():
     with pytest.raises(KeyError):
         A.timing_read("nope")
     assert A.lib().dartree_timing_read(9, C.byref(C.c_double()), C.byref(C.c_int64())) == DT_EINVAL
+
+
+def test_hbm_read_probe_validation():
+    L = A.lib()
+    probe = L.hbm_read_probe
+    assert probe(1 << 20, 16, None, None) == DT_EINVAL            # no output
+    assert probe(None, 16, 1 << 20, None) == DT_EINVAL            # no buffer
+    assert probe(1 << 20, 12, 1 << 21, None) == DT_EINVAL         # not whole 64-bit words
+    assert probe((1 << 20) + 8, 16, 1 << 21, None) == DT_EINVAL   # not 16-byte aligned

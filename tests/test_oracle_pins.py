@@ -772,3 +772,36 @@ def test_attention_prefix_and_tree_mask_match_sdpa_with_gqa():
     ref = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(q).permute(1, 0, 2), K, Vv, attn_mask=vis, scale=0.17)
     assert np.max(np.abs(out - ref.permute(1, 0, 2).numpy())) < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# read-probe checksum
+# ----------------------------------------------------------------------------
+def test_word_sum64_closed_forms():
+    # words 0 .. n-1: n (n - 1) / 2, reduced modulo 2^64 only by the definition
+    n = 1_000_003
+    assert O.word_sum64(np.arange(n, dtype=np.uint64)) == n * (n - 1) // 2 % 2 ** 64
+    # all-ones bytes: n words of 2^64 - 1 sum to -n modulo 2^64
+    assert O.word_sum64(b"\xff" * (8 * n)) == (-n) % 2 ** 64
+    # large words wrap: 2^63 + 2^63 = 0
+    assert O.word_sum64(np.array([2 ** 63, 2 ** 63], np.uint64)) == 0
+    assert O.word_sum64(b"") == 0
+    with pytest.raises(ValueError):
+        O.word_sum64(b"\x00" * 12)
+
+
+def test_word_sum64_byte_order_and_brute_force():
+    # little-endian: byte j of a word weighs 256^j
+    assert O.word_sum64(bytes([1, 2, 0, 0, 0, 0, 0, 0])) == 1 + 2 * 256
+    assert O.word_sum64(bytes([0] * 7 + [1])) == 2 ** 56
+    rng = np.random.default_rng(7)
+    raw = rng.integers(0, 256, 8 * 1001, dtype=np.uint8).tobytes()
+    want = 0
+    for i in range(0, len(raw), 8):
+        w = 0
+        for j in range(8):
+            w += raw[i + j] << (8 * j)
+        want = (want + w) % 2 ** 64
+    assert O.word_sum64(raw) == want
+    # any dtype is read as its bytes
+    assert O.word_sum64(np.frombuffer(raw, np.uint16)) == want
