@@ -41,17 +41,15 @@ int kmax_for(int k, bool greedy) {
 }
 
 // Split count for a split-K GEMM of K (nk chunks) over `tiles` column
-// tiles: the largest divisor s of nk with at most 640 workgroups and fp32
-// partial traffic (written and read: 8 s Mp bytes per column) at most a
-// quarter of the weight bytes (2 K per column).
-// 64 or more rows: up to 1280 workgroups and half the weight bytes (the
-// MFMA work per byte is high, so more workgroups pay off).
+// tiles: the largest divisor s of nk with at most 640 workgroups (1280 from
+// 64 rows, where the MFMA work per byte is high, so more workgroups pay off)
+// and fp32 partial traffic (written and read: 8 s Mp bytes per column) at
+// most a quarter of the weight bytes (2 K per column).
 int choose_splits(int nk, int tiles, int Mp, int K) {
   const long cap = Mp >= 64 ? 1280 : 640;
-  const long div = Mp >= 64 ? 2 : 4;
   int best = 1;
   for (int s = 1; s <= nk; ++s)
-    if (nk % s == 0 && (long)tiles * s <= cap && 4L * div * s * Mp <= K) best = s;
+    if (nk % s == 0 && (long)tiles * s <= cap && 16L * s * Mp <= K) best = s;
   return best;
 }
 
