@@ -14,11 +14,17 @@
 //   * the weight tiles of one 32-K step are loaded once per workgroup, each wave
 //     a quarter of them, straight into one of four LDS slots (buffer loads with
 //     the LDS bit) three steps ahead, and all four waves read them from there as
-//     MFMA operands.  Each slot is its own LDS array, so the compiler can tell a
+//     MFMA operands; each wave's activation fragments are requested two steps
+//     ahead, before that step's weights (the vector memory counter completes
+//     in issue order, so waiting for an activation never waits for weights
+//     requested later).  Each slot is its own LDS array, so the compiler can tell a
 //     read of one slot from a load into another and never waits for loads
 //     still in flight to later slots; before each barrier a wave waits (an
 //     explicit count) only for its loads into the next step's slot;
-//   * v_mfma_f32_32x32x16_bf16 with the hi/lo activation split.
+//   * v_mfma_f32_32x32x16_bf16 with the hi/lo activation split; a slice one
+//     tile short of the maximum runs a loop without the padding tile's MFMAs,
+//     and the longer slices take the lowest workgroup indices so that they
+//     are spread one per unit.
 // Operand layout (both from 16-row x 32-K packed blocks): lane l takes row
 // 16 ((l % 32) / 16) + l % 16 of a 32-row pair of blocks and, in K step st of
 // the block, K values 16 st + 8 (l / 32) .. + 8, i.e. block lane
@@ -38,7 +44,6 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int R8_WAVES = 4;                                     // one per 32-row tile
 constexpr int R8_NCMAX = 10;                                    // 32-column tiles per slice at most
-constexpr int R8_AHEAD = 3;                                     // K steps of weights in flight
 constexpr int R8_BLK = 512;                                     // bf16 per 1 KB fragment
 constexpr int R8_ACT = 4;                                       // activation loads per step
 constexpr int R8_PER_CU = 2;                                    // resident workgroups per unit
@@ -80,14 +85,18 @@ struct R8Cfg {
 // tb .. tb + T - 1 (T <= NC; 32 columns each) over K blocks kb0 .. kb0 + nkb
 // - 1 (32 K each, nkb % 4 == 0).  W is a packed bf16 matrix (grouped layout)
 // of nrows_pad rows and K columns; A the packed hi/lo planes of 128 rows.
-// Ws0..Ws3 are the workgroup's four LDS slots (distinct arrays).  TAG makes
-// the instantiation (and its lambdas) distinct per kernel: host stubs of
-// kernels that share one instantiation are not all emitted.
-template <int NC, int TAG>
+// Ws holds the workgroup's NSLOT LDS slots, each its own array; weights run
+// NSLOT - 1 steps ahead.  Only the first NCR tiles are computed (NCR < NC
+// leaves the last tiles' accumulators at zero; their fragments are still
+// loaded, so the load counts do not depend on NCR).  TAG makes the
+// instantiation (and its lambdas) distinct per kernel: host stubs of kernels
+// that share one instantiation are not all emitted.
+template <int NC, int NCR, int TAG, int NSLOT>
 __device__ __forceinline__ void r8_mainloop(const uint16_t* W, int nrows_pad, int K,
                                             const PackedA& pa, int tb, int T, int kb0, int nkb,
-                                            f32x16 (&acc)[NC], uint16_t* Ws0, uint16_t* Ws1,
-                                            uint16_t* Ws2, uint16_t* Ws3) {
+                                            f32x16 (&acc)[NC], uint16_t* const (&Ws)[NSLOT]) {
+  static_assert(NCR <= NC, "tiles computed <= tiles loaded");
+  constexpr int AHEAD = NSLOT - 1;
   using C = R8Cfg<NC>;
   constexpr int FPW = C::FPW;
   const int lane = threadIdx.x & 63;
@@ -132,15 +141,15 @@ __device__ __forceinline__ void r8_mainloop(const uint16_t* W, int nrows_pad, in
           16, w_lane, wsoff[i] + kb * 8 * R8_BLK * 2, 0, 2 /* nt */);
   };
   // R8_ACT loads of step kb's activation fragments into registers
-  u32x4 areg[R8_ACT];                                            // [st * 2 + hl]
-  auto load_a = [&](int kb) {
+  u32x4 areg[2][R8_ACT];                                         // [kb % 2][st * 2 + hl]
+  auto load_a = [&](u32x4 (&dst)[R8_ACT], int kb) {
     kb = min(kb, kb_last);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int so = a_wave + (kb * R8_BLK + 256 * st) * 2;
-      areg[2 * st] =
+      dst[2 * st] =
           __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(hrs, a_lane, so, 0));
-      areg[2 * st + 1] =
+      dst[2 * st + 1] =
           __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(lrs, a_lane, so, 0));
     }
   };
@@ -150,35 +159,50 @@ __device__ __forceinline__ void r8_mainloop(const uint16_t* W, int nrows_pad, in
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
 
-  // Per step, each wave issues FPW weight loads then R8_ACT activation loads,
-  // and no other vector memory operation.  Before the barrier that ends step
-  // kb a wave needs its loads into step kb + 1's slot to be done (issued three
-  // steps earlier).  The wait below asks for one step more: everything up to
-  // the weight loads of step kb + 2, after which only WAIT_AFTER loads were
-  // issued, so a count that is off by less than a step stays safe.
-  constexpr int WAIT_AFTER = FPW + 2 * R8_ACT;
+  // Per step kb each wave issues R8_ACT activation loads for step kb + 2,
+  // then FPW weight loads for step kb + AHEAD, and no other vector memory
+  // operation.  The vector memory counter completes in issue order, so the
+  // activation is requested before the weights: waiting for it never waits for
+  // weights issued later.  Before the barrier that ends step kb a wave needs its
+  // loads into step kb + 1's slot to be done.  The prologue issues W(kb0) ..
+  // W(kb0 + AHEAD - 3), A(kb0), W(kb0 + AHEAD - 2), A(kb0 + 1),
+  // W(kb0 + AHEAD - 1), so the loads issued after W(kb + 1) number
+  // (AHEAD - 1) (FPW + R8_ACT) in the steady state and at least
+  // (AHEAD - 1) FPW + min(3, AHEAD - 1) R8_ACT in the first steps; the wait
+  // uses that smallest count, exact where it matters and never too lax.
+  static_assert(AHEAD >= 3, "activation two steps ahead of at least three weight steps");
+  constexpr int WAIT_AFTER = (AHEAD - 1) * FPW + (AHEAD - 1 < 3 ? AHEAD - 1 : 3) * R8_ACT;
   static_assert(WAIT_AFTER < 64, "vmcnt range");
   constexpr int WAITCNT = (WAIT_AFTER & 15) | ((WAIT_AFTER >> 4) << 14) | (7 << 4) | (15 << 8);
 
-  // prologue: steps 0 .. 2 requested, steps 0 and 1 complete everywhere
-  load_w(Ws0, kb0);
-  load_w(Ws1, kb0 + 1);
-  load_w(Ws2, kb0 + 2);
-  load_a(kb0);
-  __builtin_amdgcn_s_waitcnt((R8_ACT + FPW) | (7 << 4) | (15 << 8));
+  // prologue, as if steps kb0 - AHEAD .. kb0 - 1 had run; then W(kb0)
+  // complete (issued after it: AHEAD - 1 weight steps and two activation steps)
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) {
+    if (i == AHEAD - 2) load_a(areg[0], kb0);
+    if (i == AHEAD - 1) load_a(areg[1], kb0 + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(Ws[i], kb0 + i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  constexpr int PRO = (AHEAD - 1) * FPW + 2 * R8_ACT;
+  static_assert(PRO < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((PRO & 15) | ((PRO >> 4) << 14) | (7 << 4) | (15 << 8));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
-  // one K step: request step kb + 3 into the slot freed by step kb - 1 and the
-  // activation of step kb + 1, run the MFMAs of step kb from its slot
-  auto step = [&](int kb, uint16_t* cur, uint16_t* ahead) {
-    load_w(ahead, kb + R8_AHEAD);
+  // one K step: request A(kb + 2) into the registers A(kb) leaves and
+  // W(kb + AHEAD) into the slot freed by step kb - 1, then run the MFMAs of
+  // step kb from its slot
+  auto step = [&](int kb, uint16_t* cur, uint16_t* ahead, int par) {
     u32x4 acur[R8_ACT];
 #pragma unroll
-    for (int i = 0; i < R8_ACT; ++i) acur[i] = areg[i];
+    for (int i = 0; i < R8_ACT; ++i) acur[i] = areg[par][i];
     __builtin_amdgcn_sched_barrier(0);
-    load_a(kb + 1);
+    load_a(areg[par], kb + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(ahead, kb + AHEAD);
     __builtin_amdgcn_sched_barrier(0);
     const uint16_t* slot = cur + lane * 8;
 #pragma unroll
@@ -186,20 +210,20 @@ __device__ __forceinline__ void r8_mainloop(const uint16_t* W, int nrows_pad, in
       const bf16x8 ahi = __builtin_bit_cast(bf16x8, acur[2 * st]);
       const bf16x8 alo = __builtin_bit_cast(bf16x8, acur[2 * st + 1]);
 #pragma unroll
-      for (int g = 0; g < NC; g += 4) {
+      for (int g = 0; g < NCR; g += 4) {
         bf16x8 w[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (g + q < NC)
+          if (g + q < NCR)
             w[q] = __builtin_bit_cast(bf16x8,
                                       *(const u32x4*)(slot + (2 * (g + q) + st) * R8_BLK));
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (g + q < NC)
+          if (g + q < NCR)
             acc[g + q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[q], ahi, acc[g + q], 0, 0, 0);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (g + q < NC)
+          if (g + q < NCR)
             acc[g + q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w[q], alo, acc[g + q], 0, 0, 0);
       }
     }
@@ -209,12 +233,12 @@ __device__ __forceinline__ void r8_mainloop(const uint16_t* W, int nrows_pad, in
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // nkb % 4 == 0: the slot of step kb0 + i is i % 4, static in the unrolled body
-  for (int kb = kb0; kb <= kb_last; kb += 4) {
-    step(kb, Ws0, Ws3);
-    step(kb + 1, Ws1, Ws0);
-    step(kb + 2, Ws2, Ws1);
-    step(kb + 3, Ws3, Ws2);
+  // nkb % NSLOT == 0 (NSLOT even): the slot of step kb0 + i is i % NSLOT and
+  // its activation registers i % 2, static in the unrolled body
+  for (int kb = kb0; kb <= kb_last; kb += NSLOT) {
+#pragma unroll
+    for (int i = 0; i < NSLOT; ++i)
+      step(kb + i, Ws[i], Ws[(i + NSLOT - 1) % NSLOT], i & 1);
   }
   // loads past the last step may still be landing in LDS: let them finish
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
@@ -233,13 +257,24 @@ void k_head_rows128(HeadArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x, slice = blockIdx.x;
   const int nt = (p.V + 31) / 32;
-  const int tb = (int)((long)slice * nt / G);
-  const int T = (int)((long)(slice + 1) * nt / G) - tb;         // 1 .. R8_NCMAX
+  // slices one tile longer come first, so that they are the first workgroups
+  // placed on the units (dispatched first, they spread over distinct units)
+  const int base = nt / G, extra = nt % G;
+  const int tb = slice * base + min(slice, extra);
+  const int T = base + (slice < extra ? 1 : 0);                   // 1 .. R8_NCMAX
   const int hh = lane >> 5;
   const int vpad = (p.V + PACK_ROWS - 1) / PACK_ROWS * PACK_ROWS;
   f32x16 acc[R8_NCMAX];
-  r8_mainloop<R8_NCMAX, KMAX>((const uint16_t*)p.Ut, vpad, p.d, p.pa, tb, T, 0, p.d / 32, acc,
-                              Ws0, Ws1, Ws2, Ws3);
+  uint16_t* const Ws[4] = {Ws0, Ws1, Ws2, Ws3};
+  if (T == R8_NCMAX - 1) {
+    // one tile short of the maximum: its MFMAs are not run (the loads, and so
+    // the LDS layout and the wait counts, stay those of R8_NCMAX tiles)
+    r8_mainloop<R8_NCMAX, R8_NCMAX - 1, KMAX, 4>((const uint16_t*)p.Ut, vpad, p.d, p.pa, tb, T,
+                                                 0, p.d / 32, acc, Ws);
+  } else {
+    r8_mainloop<R8_NCMAX, R8_NCMAX, KMAX, 4>((const uint16_t*)p.Ut, vpad, p.d, p.pa, tb, T, 0,
+                                             p.d / 32, acc, Ws);
+  }
 
   // per-row statistics of the slice: lanes l and l ^ 32 hold the same row
   const float scale = p.greedy ? 1.f : p.inv_T;
@@ -310,8 +345,9 @@ void k_gemm_rows128(GemmArgs g) {
   const int nkb = g.K / 32 / g.splits;
   const int npad = (g.N + PACK_ROWS - 1) / PACK_ROWS * PACK_ROWS;
   f32x16 acc[R8_GEMM_NC];
-  r8_mainloop<R8_GEMM_NC, 0>((const uint16_t*)g.Wt, npad, g.K, g.pa, tb, T, split * nkb, nkb,
-                             acc, Ws0, Ws1, Ws2, Ws3);
+  uint16_t* const Ws[4] = {Ws0, Ws1, Ws2, Ws3};
+  r8_mainloop<R8_GEMM_NC, R8_GEMM_NC, 0, 4>((const uint16_t*)g.Wt, npad, g.K, g.pa, tb, T,
+                                            split * nkb, nkb, acc, Ws);
   // element e of lane l in tile c: row l % 32 of the wave, column
   // 32 (tb + c) + 8 (e / 4) + 4 (l / 32) + e % 4
   const int row = 32 * wave + (lane & 31);
