@@ -21,6 +21,7 @@ namespace dt {
 // S range results by a butterfly and writes the row's children.  Every
 // combination follows a fixed tree, so the result does not depend on timing.
 constexpr int MERGE_THREADS = 256;
+constexpr int MERGE_TILES = 128;           // slices per merge range at least
 
 template <int KMAX>
 __global__ __launch_bounds__(MERGE_THREADS) void k_merge_part(const float2* __restrict__ ms_part,
@@ -38,6 +39,22 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_merge_part(const float2* __re
   TopK<KMAX> tk;
   tk.clear();
   const float2* mrow = ms_part + (long)row * ntiles;
+  // keys of the range: words [w_lo, w_hi) of the row's array, read as
+  // aligned pairs where possible; the first chunk is requested before the
+  // statistics are combined, so both arrive in one round trip
+  const uint64_t* krow = key_part + (long)row * ntiles * kt;
+  long w_lo = (long)t_lo * kt;
+  const long w_hi = (long)t_hi * kt;
+  const bool head_word = ((uintptr_t)(krow + w_lo) & 15) != 0 && w_lo < w_hi;
+  if (head_word) ++w_lo;
+  const long np = (w_hi - w_lo) / 2;
+  const ulonglong2* kp = (const ulonglong2*)(krow + w_lo);
+  ulonglong2 v[BATCH];
+#pragma unroll
+  for (int b = 0; b < BATCH; ++b) {
+    const long f = b * MERGE_THREADS + tid;
+    v[b] = f < np ? kp[f] : make_ulonglong2(0ull, 0ull);
+  }
   for (int t0 = t_lo; t0 < t_hi; t0 += MERGE_THREADS * BATCH) {
     float2 p[BATCH];
 #pragma unroll
@@ -48,23 +65,14 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_merge_part(const float2* __re
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) ms.combine(p[b].x, p[b].y);
   }
-  // keys of the range: words [w_lo, w_hi) of the row's array, read as
-  // aligned pairs where possible
-  const uint64_t* krow = key_part + (long)row * ntiles * kt;
-  long w_lo = (long)t_lo * kt;
-  const long w_hi = (long)t_hi * kt;
-  if (((uintptr_t)(krow + w_lo) & 15) != 0 && w_lo < w_hi) {
-    if (tid == 0) tk.insert(krow[w_lo]);
-    ++w_lo;
-  }
-  const long np = (w_hi - w_lo) / 2;
-  const ulonglong2* kp = (const ulonglong2*)(krow + w_lo);
+  if (head_word && tid == 0) tk.insert(krow[w_lo - 1]);
   for (long f0 = 0; f0 < np; f0 += MERGE_THREADS * BATCH) {
-    ulonglong2 v[BATCH];
+    if (f0 > 0) {
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b) {
-      const long f = f0 + b * MERGE_THREADS + tid;
-      v[b] = f < np ? kp[f] : make_ulonglong2(0ull, 0ull);
+      for (int b = 0; b < BATCH; ++b) {
+        const long f = f0 + b * MERGE_THREADS + tid;
+        v[b] = f < np ? kp[f] : make_ulonglong2(0ull, 0ull);
+      }
     }
 #pragma unroll
     for (int b = 0; b < BATCH; ++b) {
@@ -170,7 +178,7 @@ hipError_t launch_merge_part(const float2* ms_part, const uint64_t* key_part, in
 }
 
 int merge_splits(int ntiles) {
-  const int s = ntiles / 128;
+  const int s = ntiles / MERGE_TILES;
   return s < 1 ? 1 : (s > MERGE_SPLITS_MAX ? MERGE_SPLITS_MAX : s);
 }
 
@@ -268,7 +276,9 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_step(BeamArgs b) {
   }
   int S2 = 1;
   while (S2 < b.S) S2 <<= 1;
-  for (int i = wave; b.ms2 && i < n_prev; i += BEAM_THREADS / 64) {
+  // every row of the request is read (rows past n_prev are ignored below), so
+  // these loads need not wait for n_valid
+  for (int i = wave; b.ms2 && i < b.W; i += BEAM_THREADS / 64) {
     const long o = (long)(base + i) * b.S + lane;
     MaxSum tot{-INFINITY, 0.f};
     TopK<KMAX> all;
@@ -279,6 +289,8 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_step(BeamArgs b) {
 #pragma unroll
       for (int q = 0; q < KMAX; ++q) all.v[q] = b.key2[o * KMAX + q];
     }
+    const float sp = b.score_in[base + i];
+    if (i >= n_prev) continue;
     for (int off = 1; off < S2; off <<= 1) {
       const float m2 = __shfl_xor(tot.m, off, 64);
       const float s2 = __shfl_xor(tot.s, off, 64);
@@ -287,7 +299,6 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_step(BeamArgs b) {
     all.reduce_lanes(S2);
     if (lane == 0) {
       const float L = b.greedy ? tot.m : tot.m + logf(tot.s);
-      const float sp = b.score_in[base + i];
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
         if (j < keff) {
