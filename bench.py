@@ -200,12 +200,18 @@ def main():
     # the full steps again with every library launch bracketed by HIP events
     pk_ms, _, _ = timed_region(step, True)
     kern = {}
-    for name in ("gemm1", "gemm2", "reduce", "head", "merge_select", "attention"):
+    for name in ("gemm1", "gemm2", "reduce", "head", "merge_select", "attention", "build_small"):
         tot, n = A.timing_read(name)
         kern[name] = dict(launches=n, avg_us=(tot * 1e3 / n) if n else None)
-    head_us = kern["head"]["avg_us"]
     wbytes = 2 if wl.wdtype == "bf16" else 4
-    head_bytes = wbytes * wl.d * wl.V          # the output head, streamed once per launch
+    one_launch = kern["head"]["launches"] == 0 and kern["build_small"]["launches"] > 0
+    if one_launch:
+        # a small fp32 head built in one launch: every depth reads U, W1 and W2
+        head_us = kern["build_small"]["avg_us"]
+        head_bytes = D * wbytes * (wl.d * wl.V + 8 * wl.d * wl.d)
+    else:
+        head_us = kern["head"]["avg_us"]
+        head_bytes = wbytes * wl.d * wl.V      # the output head, streamed once per launch
     achieved = head_bytes / (head_us * 1e-6) / 1e9
     log(f"[bench] head kernel {head_us:.1f} us/launch -> {achieved:.0f} GB/s; "
         f"per-kernel timed region {pk_ms / args.steps:.3f} ms/step")
@@ -240,7 +246,9 @@ def main():
     attn_flops = 4.0 * B * (VERIFY["P"] + B) * VERIFY["hd"] * VERIFY["Hq"]
     attn_us = kern["attention"]["avg_us"]
     rows_p = next(m for m in (16, 32, 64, 128) if m >= R * W)   # padded batch rows
-    if wl.wdtype != "bf16" or rows_p < 64:
+    if one_launch:
+        head_kernel = "k_build_small: all depths of the build in one launch"
+    elif wl.wdtype != "bf16" or rows_p < 64:
         head_kernel = "k_head_bf16" if wl.wdtype == "bf16" else "k_head_f32"
     elif rows_p == 64:
         head_kernel = "k_head_wide (64 columns per wave, 64 rows)"
@@ -268,7 +276,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": profiled_traffic(wl.name),
-                     "kernel": f"corrected-logit head ({head_kernel})",
+                     "kernel": (head_kernel if one_launch
+                                else f"corrected-logit head ({head_kernel})"),
                      "bytes_per_launch": head_bytes,
                      "probe_gbs": probe["gbs"],
                      "frac_of_probe": round(achieved / probe["gbs"], 4)},

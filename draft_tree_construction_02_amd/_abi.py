@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libdartree.so")
 DT_F32, DT_BF16 = 0, 1
 DT_LAYOUT_ROWMAJOR, DT_LAYOUT_PACKED = 0, 1
 KERNEL_CLASSES = {"gemm1": 0, "gemm2": 1, "head": 2, "merge_select": 3, "reduce": 4,
-                  "attention": 5}
+                  "attention": 5, "build_small": 6}
 
 # every symbol include/dartree.h declares
 EXPORTS = [
@@ -35,7 +35,7 @@ EXPORTS = [
 ]
 
 
-DT_BUILD_MARKOV, DT_BUILD_BASE_CANDIDATES = 1, 2
+DT_BUILD_MARKOV, DT_BUILD_BASE_CANDIDATES, DT_BUILD_MULTI_KERNEL = 1, 2, 4
 
 
 class dt_build_opts(C.Structure):
@@ -188,22 +188,24 @@ def build_supertree_workspace_size(head: Head, R, D, W, k) -> int:
     return int(lib().build_supertree_workspace_size(head.ref, R, D, W, k))
 
 
-def _opts(markov: bool, n_cand: int):
-    if not markov and not n_cand:
+def _opts(markov: bool, n_cand: int, multi_kernel: bool = False):
+    if not markov and not n_cand and not multi_kernel:
         return None
     return dt_build_opts((DT_BUILD_MARKOV if markov else 0) |
-                         (DT_BUILD_BASE_CANDIDATES if n_cand else 0), int(n_cand))
+                         (DT_BUILD_BASE_CANDIDATES if n_cand else 0) |
+                         (DT_BUILD_MULTI_KERNEL if multi_kernel else 0), int(n_cand))
 
 
 def build_supertree(head: Head, h, s0, root_tok, D: int, W: int, k: int, T: float,
                     workspace=None, out=None, stream=None, markov: bool = False,
-                    n_cand: int = 0) -> dict:
+                    n_cand: int = 0, multi_kernel: bool = False) -> dict:
     """Depth-wise batched supertree construction of R requests.
 
     h [R][D][d] f32, s0 [R][d] f32, root_tok [R] int32 -> dict of pool_tok,
     pool_parent, pool_score ([R][D][W]) and n_valid ([R][D]).  markov / n_cand
     select the variants of build_supertree_ex (Markov head; children among
-    the depth's n_cand base-logit candidates)."""
+    the depth's n_cand base-logit candidates); multi_kernel runs a small fp32
+    head through the per-depth kernels instead of the one-launch build."""
     R = s0.shape[0]
     _dev(h, torch.float32, "h", (R, D, head.d))
     _dev(s0, torch.float32, "s0", (R, head.d))
@@ -214,7 +216,7 @@ def build_supertree(head: Head, h, s0, root_tok, D: int, W: int, k: int, T: floa
                    pool_parent=torch.empty((R, D, W), dtype=torch.int32, device=dev),
                    pool_score=torch.empty((R, D, W), dtype=torch.float32, device=dev),
                    n_valid=torch.empty((R, D), dtype=torch.int32, device=dev))
-    opts = _opts(markov, n_cand)
+    opts = _opts(markov, n_cand, multi_kernel)
     if opts is None:
         need = build_supertree_workspace_size(head, R, D, W, k)
         ws = _workspace(need, dev, workspace)

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libdartree.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["dartree.hip", "gemm.hip", "head_wide.hip", "select.hip", "pack.hip", "attention.hip",
-           "sequential.hip", "verify.hip", "head_rows128.hip", "probe.hip"]
+           "sequential.hip", "verify.hip", "head_rows128.hip", "probe.hip", "build_small.hip"]
 ARCH = os.environ.get("DARTREE_ARCH", "gfx950")
 
 FLAGS = [

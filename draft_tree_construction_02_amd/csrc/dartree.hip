@@ -398,7 +398,8 @@ struct BuildWs {
 
 int build_opts_ok(const dt_head* head, int k, const dt_build_opts* o) {
   if (!o) return DT_OK;
-  if (o->flags & ~(DT_BUILD_MARKOV | DT_BUILD_BASE_CANDIDATES)) return DT_EINVAL;
+  if (o->flags & ~(DT_BUILD_MARKOV | DT_BUILD_BASE_CANDIDATES | DT_BUILD_MULTI_KERNEL))
+    return DT_EINVAL;
   if (o->flags & DT_BUILD_BASE_CANDIDATES) {
     if (o->n_cand < k || o->n_cand > head->V) return DT_EINVAL;
     if (o->n_cand > DT_MAX_K) return DT_EUNSUPPORTED;
@@ -446,13 +447,30 @@ int build_supertree_ex(const dt_head* head, const float* h, const float* s0,
   const size_t need = build_supertree_ex_workspace_size(head, R, D, W, k, opts);
   if (!workspace || workspace_bytes < need) return DT_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;
+  const bool greedy = T == 0.f, bf = head->wdtype == DT_BF16;
+  const bool markov = opts && (opts->flags & DT_BUILD_MARKOV);
+  const bool base = opts && (opts->flags & DT_BUILD_BASE_CANDIDATES);
+  if (!bf && head->layout == DT_LAYOUT_ROWMAJOR && !markov && !base &&
+      !(opts && (opts->flags & DT_BUILD_MULTI_KERNEL))) {
+    // a head small enough for one workgroup's LDS: all depths in one launch
+    SmallBuildArgs sa;
+    sa.E = head->E; sa.W1t = head->W1t; sa.W2t = head->W2t; sa.Ut = head->Ut;
+    sa.d = head->d; sa.V = head->V;
+    sa.h = h; sa.s0 = s0; sa.root_tok = root_tok;
+    sa.R = R; sa.D = D; sa.W = W; sa.k = k; sa.kmax = kmax_for(k, greedy);
+    sa.greedy = greedy;
+    sa.inv_T = greedy ? 1.f : (float)(1.0 / (double)T);
+    sa.pool_tok = pool_tok; sa.pool_parent = pool_parent; sa.pool_score = pool_score;
+    sa.n_valid = n_valid;
+    if (small_build_ok(sa)) {
+      const hipError_t e = timed(DT_K_BUILD_SMALL, st, [&] { return launch_build_small(sa, st); });
+      return e == hipSuccess ? DT_OK : DT_EHIP;
+    }
+  }
   Carver c(workspace);
   BuildWs bw = carve_build(c, head, R, D, W, k, opts);
   const StepWs& w = bw.w;
   const int d = head->d, rows = R * W;
-  const bool greedy = T == 0.f, bf = head->wdtype == DT_BF16;
-  const bool markov = opts && (opts->flags & DT_BUILD_MARKOV);
-  const bool base = opts && (opts->flags & DT_BUILD_BASE_CANDIDATES);
   const int n_cand = base ? opts->n_cand : 0;
 
   hipError_t e = hipSuccess;

@@ -280,6 +280,28 @@ hipError_t launch_walk_keep(const WalkArgs& a, const float* s_cur, hipStream_t s
 // Target token of every inner node from the head's greedy keys, then the walk.
 hipError_t launch_walk(const WalkArgs& a, hipStream_t st);
 
+// One-launch build of a small fp32 head (build_small.hip): one workgroup of
+// 1024 threads per request runs all D depths with the frontier in LDS.
+constexpr size_t SMALL_BUILD_LDS_MAX = 61440;   // dynamic LDS; static arrays add 1.5 KB
+struct SmallBuildArgs {
+  const void* E = nullptr;             // fp32 row-major head
+  const void* W1t = nullptr;
+  const void* W2t = nullptr;
+  const void* Ut = nullptr;
+  int d = 0, V = 0;
+  const float* h = nullptr;            // [R][D][d]
+  const float* s0 = nullptr;           // [R][d]
+  const int32_t* root_tok = nullptr;   // [R]
+  int R = 0, D = 0, W = 0, k = 0, kmax = 1, greedy = 0;
+  float inv_T = 1.f;
+  int32_t* pool_tok = nullptr;         // [R][D][W]
+  int32_t* pool_parent = nullptr;
+  float* pool_score = nullptr;
+  int32_t* n_valid = nullptr;          // [R][D]
+};
+bool small_build_ok(const SmallBuildArgs& a);
+hipError_t launch_build_small(const SmallBuildArgs& a, hipStream_t st);
+
 // Runs fn(ctx) bracketed by timing events of kernel class cls when kernel
 // timing is on (dartree_timing_enable).
 hipError_t timed_launch(int cls, hipStream_t st, hipError_t (*fn)(void*), void* ctx);

@@ -158,6 +158,9 @@ size_t build_supertree_workspace_size(const dt_head* head, int R, int D, int W, 
  *   n_valid     [R][D]    i32  used slots per depth
  * Slots are in (score desc, parent slot asc, rank asc) order.
  * Inputs must be finite.
+ * A small fp32 head (row-major, W <= 64, and the states, x, H and logits of
+ * W rows within 60 KB: 4 (7 W d + W V) + 12 W kmax bytes) is built by one
+ * launch with one workgroup per request; the workspace is then unused.
  */
 int build_supertree(const dt_head* head, const float* h, const float* s0,
                     const int32_t* root_tok, int R, int D, int W, int k, float T,
@@ -168,6 +171,8 @@ int build_supertree(const dt_head* head, const float* h, const float* s0,
 /* Build variants (dt_build_opts.flags). */
 #define DT_BUILD_MARKOV 1           /* no carried state: every update starts from s0    */
 #define DT_BUILD_BASE_CANDIDATES 2  /* children only among the depth's base candidates   */
+#define DT_BUILD_MULTI_KERNEL 4     /* same result; small fp32 heads run the per-depth   */
+                                    /* kernels instead of the one-launch build           */
 
 typedef struct {
   int32_t flags;    /* DT_BUILD_* bits                                                   */
@@ -414,7 +419,8 @@ typedef enum {
   DT_K_MERGE = 3,   /* per-row merge and per-request beam select          */
   DT_K_REDUCE = 4,  /* split-K reductions (GELU / residual epilogues)     */
   DT_K_ATTN = 5,    /* tree-attention verification layer (both kernels)   */
-  DT_K_COUNT = 6
+  DT_K_BUILD_SMALL = 6, /* one-launch build of a small fp32 head (all depths) */
+  DT_K_COUNT = 7
 } dt_kernel_class;
 
 /*

@@ -96,6 +96,58 @@ def test_build_prune_mask_match_oracle(name, packed):
     print(f"{name}: exemptions {total_exempt}", flush=True)
 
 
+def small_fp32_cases():
+    """fp32 heads small enough for the one-launch build (states, x, H and
+    logits of W rows within one workgroup's LDS)."""
+    return {
+        "tiny": synth.workloads()["tiny"],
+        # several requests, 16 children, a vocabulary that is not a multiple of
+        # 64 and a temperature other than 1
+        "f32_small_k16": synth.Workload("f32_small_k16", V=600, d=32, wdtype="f32", D=5, W=16,
+                                        k=16, B=40, beta=-0.05, T=0.8, R=3, seeds=(1, 2, 3)),
+        # greedy limit: every request's supertree is a chain
+        "f32_small_T0": synth.Workload("f32_small_T0", V=1000, d=64, wdtype="f32", D=6, W=4,
+                                       k=4, B=6, beta=0.0, T=0.0, R=2, seeds=(4, 5)),
+        # one branch, one child: the greedy chain at T = 1
+        "f32_small_W1": synth.Workload("f32_small_W1", V=513, d=128, wdtype="f32", D=8, W=1,
+                                       k=1, B=8, beta=-0.1, T=1.0, R=1, seeds=(6,)),
+    }
+
+
+@pytest.mark.parametrize("multi_kernel", [False, True])
+@pytest.mark.parametrize("name", list(small_fp32_cases()))
+def test_small_fp32_build_both_paths_match_oracle(name, multi_kernel):
+    # the one-launch build and the per-depth kernels on the same inputs; the
+    # timing class shows which one ran
+    wl = small_fp32_cases()[name]
+    print(f"case {name} multi_kernel={multi_kernel}", flush=True)
+    hw, req, head, ohead = case_inputs(wl)
+    tol, tau = tolerances(wl.wdtype)
+    h, s0, root = dev_requests(req)
+    A.timing_reset()
+    A.timing_enable(True)
+    out = A.build_supertree(head, h, s0, root, wl.D, wl.W, wl.k, wl.T, multi_kernel=multi_kernel)
+    torch.cuda.synchronize()
+    A.timing_enable(False)
+    _, n_small = A.timing_read("build_small")
+    _, n_head = A.timing_read("head")
+    assert (n_small, n_head) == ((0, wl.D) if multi_kernel else (1, 0))
+    pool = to_np(out)
+    total_exempt = 0
+    for r in range(wl.R):
+        dev = dict(tok=pool["pool_tok"][r], parent=pool["pool_parent"][r],
+                   score=pool["pool_score"][r], n_valid=pool["n_valid"][r])
+        rep = PAR.check_build(ohead, req.h[r], req.s0[r], int(req.root_tok[r]), wl.D, wl.W,
+                              wl.k, wl.T, dev, tol, tau)
+        assert rep.ok, rep.failures[:5]
+        if rep.exemptions == 0:
+            ora = O.build_supertree(ohead, req.h[r], req.s0[r], int(req.root_tok[r]), wl.D,
+                                    wl.W, wl.k, wl.T)
+            assert not PAR.compare_exact(ora, dev, tol)
+        total_exempt += rep.exemptions
+    print(f"{name}: exemptions {total_exempt}", flush=True)
+
+
 def test_packed_layout_is_the_documented_block_order():
     # the packed weights, read back, follow the block order the header states
     wl = small_cases()["bf16_ragged_rows"]          # V = 3001: padded last tile
