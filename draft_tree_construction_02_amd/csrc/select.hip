@@ -244,13 +244,14 @@ hipError_t launch_fill_rows(int rows, int Mp, const int32_t* tok_in, int32_t* to
 }
 
 // One workgroup per request, two phases.
-// 1. Children of each frontier row i (one wave per row): the row's S merge
-//    range results are folded by a butterfly into (max, sum exp) and the
-//    top-keff keys; child rank j gets logp = value - log-sum-exp (0 at T=0).
+// 1. Children of each frontier row i (16 lanes per row, four rows per wave):
+//    the row's S <= 16 merge range results are folded by a butterfly into
+//    (max, sum exp) and the top-keff keys; child rank j gets logp = value -
+//    log-sum-exp (0 at T=0).
 // 2. Candidate c = i * keff + j scores score_in[i] + logp; the
 //    n_t = min(W, n_{t-1} keff) best by (score desc, c asc) take slots
 //    0..n_t-1 in that order.  A candidate's slot is the number of candidates
-//    with a larger key (keys are distinct).
+//    with a larger key (keys are distinct), counted by several lanes each.
 constexpr int BEAM_THREADS = 1024;
 
 template <int KMAX>
@@ -276,28 +277,32 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_step(BeamArgs b) {
   }
   int S2 = 1;
   while (S2 < b.S) S2 <<= 1;
-  // every row of the request is read (rows past n_prev are ignored below), so
-  // these loads need not wait for n_valid
-  for (int i = wave; b.ms2 && i < b.W; i += BEAM_THREADS / 64) {
-    const long o = (long)(base + i) * b.S + lane;
+  // four rows per wave, one per group of 16 lanes (S <= 16 range results per
+  // row, so every butterfly stays inside its group).  Every row of the request
+  // is read (rows past n_prev are ignored below), so these loads need not
+  // wait for n_valid.
+  constexpr int RPW = WAVE / 16;
+  for (int i0 = wave * RPW; b.ms2 && i0 < b.W; i0 += (BEAM_THREADS / WAVE) * RPW) {
+    const int sl = lane & 15, i = i0 + (lane >> 4);
+    const bool row_ok = i < b.W;
+    const long o = (long)(base + (row_ok ? i : 0)) * b.S + sl;
     MaxSum tot{-INFINITY, 0.f};
     TopK<KMAX> all;
     all.clear();
-    if (lane < b.S) {
+    if (row_ok && sl < b.S) {
       const float2 e = b.ms2[o];
       tot = MaxSum{e.x, e.y};
 #pragma unroll
       for (int q = 0; q < KMAX; ++q) all.v[q] = b.key2[o * KMAX + q];
     }
-    const float sp = b.score_in[base + i];
-    if (i >= n_prev) continue;
+    const float sp = row_ok ? b.score_in[base + i] : 0.f;
     for (int off = 1; off < S2; off <<= 1) {
       const float m2 = __shfl_xor(tot.m, off, 64);
       const float s2 = __shfl_xor(tot.s, off, 64);
       tot.combine(m2, s2);
     }
     all.reduce_lanes(S2);
-    if (lane == 0) {
+    if (sl == 0 && i < n_prev) {
       const float L = b.greedy ? tot.m : tot.m + logf(tot.s);
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
@@ -313,11 +318,19 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_step(BeamArgs b) {
   }
   __syncthreads();
   const long pool = ((long)r * b.D + b.t) * b.W;
-  for (int c = tid; c < ncand; c += BEAM_THREADS) {
-    const uint64_t kc = keys[c];
+  // rank of each candidate = number of larger keys, counted by P lanes each
+  // (strided subsets of the keys, summed by a butterfly)
+  int P = 1;
+  while (P < WAVE && ncand * (2 * P) <= BEAM_THREADS) P *= 2;
+  for (int c0 = 0; c0 < ncand; c0 += BEAM_THREADS / P) {
+    const int c = c0 + tid / P, p = tid % P;
+    const bool live = c < ncand;
+    const uint64_t kc = live ? keys[c] : 0ull;
     int rank = 0;
-    for (int j = 0; j < ncand; ++j) rank += keys[j] > kc;
-    if (rank < nkeep) {
+    if (live)
+      for (int j = p; j < ncand; j += P) rank += keys[j] > kc;
+    for (int off = 1; off < P; off <<= 1) rank += __shfl_xor(rank, off, 64);
+    if (live && p == 0 && rank < nkeep) {
       const int i = c / keff;
       const int32_t tk = c_tok[c];
       const float sc = key_value(kc);
