@@ -327,8 +327,10 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_step(BeamArgs b) {
     const bool live = c < ncand;
     const uint64_t kc = live ? keys[c] : 0ull;
     int rank = 0;
-    if (live)
+    if (live) {
+#pragma unroll 8
       for (int j = p; j < ncand; j += P) rank += keys[j] > kc;
+    }
     for (int off = 1; off < P; off <<= 1) rank += __shfl_xor(rank, off, 64);
     if (live && p == 0 && rank < nkeep) {
       const int i = c / keff;
