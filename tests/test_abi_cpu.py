@@ -160,6 +160,18 @@ def test_build_supertree_ex_validation():
     assert ex(A.dt_build_opts(A.DT_BUILD_MARKOV, 0), T=-1.0) == DT_EINVAL
     assert ex(A.dt_build_opts(A.DT_BUILD_MARKOV, 0), ws=10) == DT_EWORKSPACE
     assert ex(None, k=0) == DT_EINVAL
+    # the per-depth-kernel flag: same workspace, combines with the variants,
+    # and every check still runs before any launch
+    mk = A.dt_build_opts(A.DT_BUILD_MULTI_KERNEL, 0)
+    assert L.build_supertree_ex_workspace_size(C.byref(h), 1, 16, 16, 8, C.byref(mk)) == \
+        L.build_supertree_workspace_size(C.byref(h), 1, 16, 16, 8)
+    assert ex(A.dt_build_opts(A.DT_BUILD_MULTI_KERNEL | A.DT_BUILD_MARKOV, 0), T=-1.0) == DT_EINVAL
+    assert ex(mk, ws=10) == DT_EWORKSPACE
+    assert ex(A.dt_build_opts(A.DT_BUILD_MULTI_KERNEL | 8, 0)) == DT_EINVAL
+    # a small fp32 head (one-launch build) checks its workspace as well
+    f = fake_head(d=64, V=1000, wdtype=A.DT_F32)
+    assert L.build_supertree(C.byref(f), 1, 1, 1, 1, 6, 4, 4, 1.0, 1, 1, 1, 1, 1, 10,
+                             None) == DT_EWORKSPACE
 
 
 def test_pack_head_validation():
