@@ -167,20 +167,26 @@ def test_packed_layout_is_the_documented_block_order():
         off += (Np * K * 2 + 255) // 256 * 256 // 2
 
 
-@pytest.mark.parametrize("name,packed,R,W", [("bf16_T1", True, 2, 8), ("tiny", False, 1, 4),
-                                             # 128 rows: the 128-row head and GEMM
-                                             ("bf16_T1", True, 8, 16)])
-def test_build_is_deterministic(name, packed, R, W):
+@pytest.mark.parametrize("name,packed,R,W,multi_kernel", [
+    ("bf16_T1", True, 2, 8, False),
+    # the small fp32 head: the one-launch build and the per-depth kernels
+    ("tiny", False, 1, 4, False), ("tiny", False, 1, 4, True),
+    # 128 rows: the 128-row head and GEMM
+    ("bf16_T1", True, 8, 16, False)])
+def test_build_is_deterministic(name, packed, R, W, multi_kernel):
     # ten builds of the same inputs, bit for bit (fixed-order reductions, no
     # floating-point atomics)
     wl = small_cases()[name].with_(R=R, W=W, seeds=tuple(range(30, 30 + R)))
-    print(f"determinism {name} packed={packed} rows={R * W}", flush=True)
+    print(f"determinism {name} packed={packed} rows={R * W} multi_kernel={multi_kernel}",
+          flush=True)
     hw, req = synth.make_workload_inputs(wl)
     head = dev_weights(hw, packed)
     h, s0, root = dev_requests(req)
-    ref = to_np(A.build_supertree(head, h, s0, root, wl.D, wl.W, wl.k, wl.T))
+    ref = to_np(A.build_supertree(head, h, s0, root, wl.D, wl.W, wl.k, wl.T,
+                                  multi_kernel=multi_kernel))
     for _ in range(9):
-        got = to_np(A.build_supertree(head, h, s0, root, wl.D, wl.W, wl.k, wl.T))
+        got = to_np(A.build_supertree(head, h, s0, root, wl.D, wl.W, wl.k, wl.T,
+                                      multi_kernel=multi_kernel))
         for key in ref:
             assert np.array_equal(ref[key].view(np.uint8), got[key].view(np.uint8)), key
 
