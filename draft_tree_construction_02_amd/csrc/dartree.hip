@@ -12,6 +12,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -74,6 +75,8 @@ bool head_ok(const dt_head* h) {
   return false;
 }
 
+int head_tiles_for(const dt_head* hd, int Mp);
+
 // Workspace of the state update + head for Mp rows.
 struct StepWs {
   float* part;                 // split-K partials (shared by both GEMMs)
@@ -104,6 +107,7 @@ StepWs carve_step(Carver& c, const dt_head* h, int rows, int k) {
   w.tiles1 = (4 * d + TN - 1) / TN;
   w.tiles2 = (d + TN - 1) / TN;
   w.tilesV = (V + head_tile_n(bf) - 1) / head_tile_n(bf);
+  w.tilesV = std::max(w.tilesV, head_tiles_for(h, w.Mp));   // slices of the launch, if more
   w.splits1 = choose_splits(d / KC, w.tiles1, w.Mp, d);
   w.splits2 = choose_splits(4 * d / KC, w.tiles2, w.Mp, 4 * d);
   const size_t part1 = (size_t)w.splits1 * w.Mp * 4 * d;

@@ -88,8 +88,24 @@ int gemm_gather_max_rows() { return 16 * DT_GATHER_MAX_MT; }
 
 int gemm_tile_n(int w_bf16) { return w_bf16 ? TN_GEMM : TN_F; }
 int head_tile_n(int w_bf16) { return w_bf16 ? TN_HEAD : TN_F; }
+// Balanced 16-row bf16 head: G workgroups, the smallest multiple of the
+// compute-unit count with at most 8 tiles of 16 columns each, workgroup j
+// taking tiles [j nt / G, (j + 1) nt / G) of the nt = ceil(V / 16); so every
+// unit streams the same number of workgroups and the slices differ by at most
+// one 16-column tile (1280 workgroups at V = 151936 instead of 1187 tiles of
+// 128 columns, which leave some units a fifth tile).  At 32 rows the fixed
+// 128-column tiles measured faster, so they stay.
+static bool head_bal_ok(const HeadArgs& p) {
+  return p.w_bf16 && p.Mp == 16 && !head_rows128_ok(p) && !head_wide_ok(p);
+}
+static int head_bal_groups(int V) {
+  const int nt = (V + 15) / 16, need = (nt + 7) / 8, cus = device_cu_count();
+  const int g = (need + cus - 1) / cus * cus;
+  return g <= nt ? g : need;
+}
 int head_tiles(const HeadArgs& p) {
   if (head_rows128_ok(p)) return head_rows128_slices(p);
+  if (head_bal_ok(p)) return head_bal_groups(p.V);
   const int tn = head_wide_ok(p) ? head_wide_tile_n() : head_tile_n(p.w_bf16);
   return (p.V + tn - 1) / tn;
 }
@@ -560,13 +576,13 @@ hipError_t launch_reduce(const ReduceArgs& r, hipStream_t st) {
 // corrected-logit head with fused per-tile log-softmax statistics and top-k
 // ----------------------------------------------------------------------------
 template <int MT, int KMAX, int TN, int THREADS>
-__device__ __forceinline__ void head_epilogue(const HeadArgs& p, const float* Cs, int tile) {
+__device__ __forceinline__ void head_epilogue(const HeadArgs& p, const float* Cs, int tile, int n0,
+                                              int nvalid) {
   constexpr int Mp = 16 * MT;
   constexpr int G = THREADS / Mp;         // threads per row (power of two <= 64)
   static_assert(G >= 1 && G <= 64, "row group must fit in a wave");
   const int tid = threadIdx.x, m = tid / G, q = tid % G;
-  const int n0 = tile * TN, ntiles = gridDim.x;
-  const int nvalid = min(TN, p.V - n0);
+  const int ntiles = gridDim.x;
   const float* row = Cs + m * (TN + CPAD);
   float mx = -INFINITY;
   TopK<KMAX> tk;
@@ -605,11 +621,21 @@ __attribute__((amdgpu_waves_per_eu(DT_HEAD_WPE, 8))) void k_head_bf16(HeadArgs p
   constexpr int NW = DT_NW_HEAD;
   constexpr int TN = TN_HEAD;
   __shared__ __attribute__((aligned(16))) unsigned char smem[BfCfg<MT, NBUF, NW, DT_WV_HEAD>::LDS];
-  const int tile = blockIdx.x, n0 = tile * TN;
+  const int tile = blockIdx.x;
+  // this workgroup's columns [n0, col_end): a fixed 128-column tile, or with
+  // the balanced grid a run of at most 8 tiles of 16 (columns past col_end are
+  // zero-filled by the loads, not read)
+  int n0 = tile * TN, col_end = p.V;
+  if (p.bal) {
+    const int nt = (p.V + 15) / 16, G = gridDim.x;
+    const int tb = (int)((long)tile * nt / G), te = (int)((long)(tile + 1) * nt / G);
+    n0 = 16 * tb;
+    col_end = min(16 * te, p.V);
+  }
   f32x4 acc[NW][MT];
   tile_bf16<MT, NBUF, PW, NW, DT_PF_HEAD, DT_WV_HEAD,
             AStagePacked<MT, BfCfg<MT, NBUF, NW, DT_WV_HEAD>::KC, DT_WV_HEAD>>(
-      p.pa, (const uint16_t*)p.Ut, p.V, n0, 0, p.d, smem, acc);
+      p.pa, (const uint16_t*)p.Ut, col_end, n0, 0, p.d, smem, acc);
   // accumulators -> LDS C tile (the A buffers are free after the last barrier)
   float* Cs = (float*)smem;
   const float scale = p.greedy ? 1.f : p.inv_T;
@@ -624,7 +650,7 @@ __attribute__((amdgpu_waves_per_eu(DT_HEAD_WPE, 8))) void k_head_bf16(HeadArgs p
           make_float4(v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale);
     }
   __syncthreads();
-  head_epilogue<MT, KMAX, TN, 64 * DT_WV_HEAD>(p, Cs, tile);
+  head_epilogue<MT, KMAX, TN, 64 * DT_WV_HEAD>(p, Cs, tile, n0, min(TN, col_end - n0));
 }
 
 template <int MT, int KMAX>
@@ -634,7 +660,7 @@ __global__ __launch_bounds__(NT) void k_head_f32(HeadArgs p) {
   const int tile = blockIdx.x;
   const float* Cs = tile_f32<MT, false>(p.a, (const float*)p.Ut, p.d, p.V, tile * TN_F, 0, p.d,
                                         p.greedy ? 1.f : p.inv_T, smem);
-  head_epilogue<MT, KMAX, TN_F, NT>(p, Cs, tile);
+  head_epilogue<MT, KMAX, TN_F, NT>(p, Cs, tile, tile * TN_F, min(TN_F, p.V - tile * TN_F));
 }
 
 // ----------------------------------------------------------------------------
@@ -691,6 +717,7 @@ template <int MT, int KMAX>
 static hipError_t head_mk(const HeadArgs& p, hipStream_t st) {
   const int TN = p.w_bf16 ? TN_HEAD : TN_F;
   dim3 grid((p.V + TN - 1) / TN);
+  if (p.bal) grid = dim3(head_bal_groups(p.V));
   if (p.w_bf16) {
     constexpr int NB = MT >= DT_NBUF1_MT ? 1 : 2;
     if (p.w_packed)
@@ -714,9 +741,11 @@ static hipError_t head_mt(const HeadArgs& p, hipStream_t st) {
   }
 }
 
-hipError_t launch_head(const HeadArgs& p, hipStream_t st) {
-  if (head_rows128_ok(p)) return launch_head_rows128(p, st);
-  if (head_wide_ok(p)) return launch_head_wide(p, st);
+hipError_t launch_head(const HeadArgs& p0, hipStream_t st) {
+  if (head_rows128_ok(p0)) return launch_head_rows128(p0, st);
+  if (head_wide_ok(p0)) return launch_head_wide(p0, st);
+  HeadArgs p = p0;
+  p.bal = head_bal_ok(p0) ? 1 : 0;
   switch (p.Mp) {
     case 16: return head_mt<1>(p, st);
     case 32: return head_mt<2>(p, st);

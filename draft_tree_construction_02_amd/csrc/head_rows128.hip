@@ -48,12 +48,14 @@ constexpr int R8_BLK = 512;                                     // bf16 per 1 KB
 constexpr int R8_ACT = 4;                                       // activation loads per step
 constexpr int R8_PER_CU = 2;                                    // resident workgroups per unit
 
-// Compute units of the current device, queried once per device (a stale
-// read by a concurrent first caller only repeats the query).
 constexpr int R8_MAX_DEVICES = 64;
 int g_cus[R8_MAX_DEVICES] = {};
 
-int cu_count() {
+}  // namespace
+
+// Compute units of the current device, queried once per device (a stale
+// read by a concurrent first caller only repeats the query).
+int device_cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
   if (dev < R8_MAX_DEVICES && g_cus[dev] > 0) return g_cus[dev];
@@ -62,6 +64,10 @@ int cu_count() {
   if (dev < R8_MAX_DEVICES) g_cus[dev] = n;
   return n;
 }
+
+namespace {
+
+int cu_count() { return device_cu_count(); }
 
 // Slices of the vocabulary: as many as resident workgroups, each of at most
 // R8_NCMAX tiles and at least 4 (the callers size the partials for slices of

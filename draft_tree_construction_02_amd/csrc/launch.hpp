@@ -97,7 +97,9 @@ struct HeadArgs {
   int greedy = 0;
   float2* ms_part = nullptr;  // [Mp][ntiles]
   uint64_t* key_part = nullptr;  // [Mp][ntiles][k]
+  int bal = 0;                // set by launch_head: balanced column runs (see head_tiles)
 };
+int device_cu_count();                       // compute units of the current device
 int head_tile_n(int w_bf16);                 // smallest slice width (sizes workspaces)
 int head_tiles(const HeadArgs& h);           // vocabulary slices of this launch
 hipError_t launch_head(const HeadArgs& h, hipStream_t st);
