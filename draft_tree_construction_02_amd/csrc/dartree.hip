@@ -54,6 +54,27 @@ int choose_splits(int nk, int tiles, int Mp, int K) {
   return best;
 }
 
+// Balanced split-K grid for 16-row bf16 products whose standard grid (tiles
+// of 128 columns x choose_splits) is not a multiple of the compute units:
+// runs x splits = 2 x CUs workgroups, splits a divisor of nk within the
+// partial budget, each run at most 8 tiles of 16 columns.  Returns false when
+// no such grid exists (the standard one stays).
+bool choose_runs(int nk, int N, int Mp, int K, int std_wgs, int& splits, int& runs) {
+  const int cus = device_cu_count();
+  if (Mp != 16 || N % 16 != 0 || std_wgs % cus == 0) return false;
+  const int nt = N / 16, G = 2 * cus;
+  for (int s = nk; s >= 1; --s) {
+    if (nk % s != 0 || G % s != 0 || 16L * s * Mp > K) continue;
+    const int r = G / s;
+    if (r <= nt && (nt + r - 1) / r <= 8) {
+      splits = s;
+      runs = r;
+      return true;
+    }
+  }
+  return false;
+}
+
 struct Carver {
   char* base;
   size_t off = 0;
@@ -96,6 +117,7 @@ struct StepWs {
   int32_t* src[2];
   float* S[2];                 // [Mp][d] fp32 updated states (ping-pong)
   int Mp, tiles1, tiles2, tilesV, splits1, splits2;
+  int runs1 = 0, runs2 = 0;    // balanced split-K grids (0: tiles of 128 columns)
 };
 
 StepWs carve_step(Carver& c, const dt_head* h, int rows, int k) {
@@ -110,6 +132,10 @@ StepWs carve_step(Carver& c, const dt_head* h, int rows, int k) {
   w.tilesV = std::max(w.tilesV, head_tiles_for(h, w.Mp));   // slices of the launch, if more
   w.splits1 = choose_splits(d / KC, w.tiles1, w.Mp, d);
   w.splits2 = choose_splits(4 * d / KC, w.tiles2, w.Mp, 4 * d);
+  if (bf) {
+    choose_runs(d / KC, 4 * d, w.Mp, d, w.tiles1 * w.splits1, w.splits1, w.runs1);
+    choose_runs(4 * d / KC, d, w.Mp, 4 * d, w.tiles2 * w.splits2, w.splits2, w.runs2);
+  }
   const size_t part1 = (size_t)w.splits1 * w.Mp * 4 * d;
   const size_t part2 = (size_t)w.splits2 * w.Mp * d;
   const size_t md = (size_t)w.Mp * d;
@@ -257,6 +283,7 @@ hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hip
   g1.K = d;
   g1.Mp = w.Mp;
   g1.splits = w.splits1;
+  g1.runs = w.runs1;
   g1.part = w.part;
   e = timed(DT_K_GEMM1, st, [&] { return launch_gemm(g1, st); });
   if (e != hipSuccess) return e;
@@ -288,6 +315,7 @@ hipError_t run_update(const dt_head* hd, const StepWs& w, const DepthIo& io, hip
   g2.K = 4 * d;
   g2.Mp = w.Mp;
   g2.splits = w.splits2;
+  g2.runs = w.runs2;
   g2.part = w.part;
   e = timed(DT_K_GEMM2, st, [&] { return launch_gemm(g2, st); });
   if (e != hipSuccess) return e;

@@ -468,20 +468,26 @@ __global__ __launch_bounds__(64 * DT_WV_GEMM) void k_gemm_bf16(GemmArgs g) {
   constexpr int Mp = 16 * MT;
   const int tile = blockIdx.x, split = blockIdx.y;
   const int klen = g.K / g.splits, k0 = split * klen;
-  const int n0 = tile * TN_GEMM;
+  int n0 = tile * TN_GEMM, col_end = g.N;
+  if (g.runs > 0) {
+    // a balanced run of 16-column tiles; columns past col_end are zero-filled
+    const int nt = g.N / 16;
+    n0 = 16 * (int)((long)tile * nt / g.runs);
+    col_end = 16 * (int)((long)(tile + 1) * nt / g.runs);
+  }
   f32x4 acc[NW][MT];
   if constexpr (GATHER)
     tile_bf16<MT, NBUF, PW, NW, DT_PF_GEMM, WV, AStageGather<MT, Cfg::KC, WV>>(
-        GatherA{g.a, g.K}, (const uint16_t*)g.Wt, g.N, n0, k0, klen, smem, acc);
+        GatherA{g.a, g.K}, (const uint16_t*)g.Wt, col_end, n0, k0, klen, smem, acc);
   else
     tile_bf16<MT, NBUF, PW, NW, DT_PF_GEMM, WV, AStagePacked<MT, Cfg::KC, WV>>(
-        g.pa, (const uint16_t*)g.Wt, g.N, n0, k0, klen, smem, acc);
+        g.pa, (const uint16_t*)g.Wt, col_end, n0, k0, klen, smem, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
 #pragma unroll
   for (int c = 0; c < NW; ++c) {
     const int n = n0 + wave * NW * 16 + c * 16 + 4 * q;
-    if (n >= g.N) continue;
+    if (n >= col_end) continue;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = 16 * mt + r;
@@ -675,7 +681,7 @@ __global__ __launch_bounds__(NT) void k_head_f32(HeadArgs p) {
 template <int MT>
 static hipError_t gemm_mt(const GemmArgs& g, hipStream_t st) {
   const int TN = g.w_bf16 ? TN_GEMM : TN_F;
-  dim3 grid((g.N + TN - 1) / TN, g.splits);
+  dim3 grid(g.w_bf16 && g.runs > 0 ? g.runs : (g.N + TN - 1) / TN, g.splits);
   if (g.w_bf16) {
     constexpr int NB = MT >= DT_NBUF1_MT ? 1 : 2;
     const dim3 blk(64 * DT_WV_GEMM);

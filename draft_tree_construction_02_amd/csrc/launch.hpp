@@ -54,6 +54,8 @@ struct GemmArgs {
   int N = 0, K = 0;
   int Mp = 0;                 // padded rows (16, 32, 64 or 128)
   int splits = 1;
+  int runs = 0;               // bf16, > 0: workgroup x of a split takes the 16-column tiles
+                              // [x nt / runs, (x + 1) nt / runs) (nt = N / 16, <= 8 each)
   float* part = nullptr;
 };
 
