@@ -88,15 +88,17 @@ int gemm_gather_max_rows() { return 16 * DT_GATHER_MAX_MT; }
 
 int gemm_tile_n(int w_bf16) { return w_bf16 ? TN_GEMM : TN_F; }
 int head_tile_n(int w_bf16) { return w_bf16 ? TN_HEAD : TN_F; }
-// Balanced 16-row bf16 head: G workgroups, the smallest multiple of the
+// Balanced <=32-row bf16 head: G workgroups, the smallest multiple of the
 // compute-unit count with at most 8 tiles of 16 columns each, workgroup j
 // taking tiles [j nt / G, (j + 1) nt / G) of the nt = ceil(V / 16); so every
 // unit streams the same number of workgroups and the slices differ by at most
 // one 16-column tile (1280 workgroups at V = 151936 instead of 1187 tiles of
-// 128 columns, which leave some units a fifth tile).  At 32 rows the fixed
-// 128-column tiles measured faster, so they stay.
+// 128 columns, which leave some units a fifth tile).  At 32 rows the
+// activation chunk is single-buffered on this grid: double-buffered, five
+// workgroups would need all of a unit's 160 KB of LDS and a fifth round of
+// workgroups would trail.
 static bool head_bal_ok(const HeadArgs& p) {
-  return p.w_bf16 && p.Mp == 16 && !head_rows128_ok(p) && !head_wide_ok(p);
+  return p.w_bf16 && (p.Mp == 16 || p.Mp == 32) && !head_rows128_ok(p) && !head_wide_ok(p);
 }
 static int head_bal_groups(int V) {
   const int nt = (V + 15) / 16, need = (nt + 7) / 8, cus = device_cu_count();
@@ -726,7 +728,14 @@ static hipError_t head_mk(const HeadArgs& p, hipStream_t st) {
   if (p.bal) grid = dim3(head_bal_groups(p.V));
   if (p.w_bf16) {
     constexpr int NB = MT >= DT_NBUF1_MT ? 1 : 2;
-    if (p.w_packed)
+    if (MT == 2 && p.bal) {
+      // balanced 32-row grid: one activation buffer, so that five workgroups
+      // fit in a unit's LDS
+      if (p.w_packed)
+        hipLaunchKernelGGL((k_head_bf16<MT, 1, KMAX, true>), grid, dim3(64 * DT_WV_HEAD), 0, st, p);
+      else
+        hipLaunchKernelGGL((k_head_bf16<MT, 1, KMAX, false>), grid, dim3(64 * DT_WV_HEAD), 0, st, p);
+    } else if (p.w_packed)
       hipLaunchKernelGGL((k_head_bf16<MT, NB, KMAX, true>), grid, dim3(64 * DT_WV_HEAD), 0, st, p);
     else
       hipLaunchKernelGGL((k_head_bf16<MT, NB, KMAX, false>), grid, dim3(64 * DT_WV_HEAD), 0, st, p);
