@@ -94,9 +94,9 @@ int head_tile_n(int w_bf16) { return w_bf16 ? TN_HEAD : TN_F; }
 // unit streams the same number of workgroups and the slices differ by at most
 // one 16-column tile (1280 workgroups at V = 151936 instead of 1187 tiles of
 // 128 columns, which leave some units a fifth tile).  At 32 rows the
-// activation chunk is single-buffered on this grid: double-buffered, five
-// workgroups would need all of a unit's 160 KB of LDS and a fifth round of
-// workgroups would trail.
+// activation chunk is single-buffered on this grid, the form that measured
+// faster there (double-buffered, the balanced grid was slower than the fixed
+// tiles).
 static bool head_bal_ok(const HeadArgs& p) {
   return p.w_bf16 && (p.Mp == 16 || p.Mp == 32) && !head_rows128_ok(p) && !head_wide_ok(p);
 }
@@ -729,8 +729,7 @@ static hipError_t head_mk(const HeadArgs& p, hipStream_t st) {
   if (p.w_bf16) {
     constexpr int NB = MT >= DT_NBUF1_MT ? 1 : 2;
     if (MT == 2 && p.bal) {
-      // balanced 32-row grid: one activation buffer, so that five workgroups
-      // fit in a unit's LDS
+      // balanced 32-row grid: one activation buffer (measured faster here)
       if (p.w_packed)
         hipLaunchKernelGGL((k_head_bf16<MT, 1, KMAX, true>), grid, dim3(64 * DT_WV_HEAD), 0, st, p);
       else
