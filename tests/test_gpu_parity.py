@@ -37,6 +37,10 @@ def small_cases():
                                    B=40, beta=-0.2, T=1.3, R=1, seeds=(7,)),
         "f32_wide": synth.Workload("f32_wide", V=700, d=96, wdtype="f32", D=4, W=40, k=5, B=100,
                                    beta=-0.01, T=1.0, R=2, seeds=(2, 9)),
+        # 16 rows at d = 1024: both state-update products take the balanced
+        # split-K grid (runs x splits = 2 x CUs), the head its balanced grid
+        "bf16_d1024": synth.Workload("bf16_d1024", V=4000, d=1024, wdtype="bf16", D=3, W=8, k=4,
+                                     B=12, beta=-0.05, T=1.0, R=2, seeds=(11, 12)),
     }
 
 
@@ -172,7 +176,9 @@ def test_packed_layout_is_the_documented_block_order():
     # the small fp32 head: the one-launch build and the per-depth kernels
     ("tiny", False, 1, 4, False), ("tiny", False, 1, 4, True),
     # 128 rows: the 128-row head and GEMM
-    ("bf16_T1", True, 8, 16, False)])
+    ("bf16_T1", True, 8, 16, False),
+    # the balanced split-K grid of 16-row products
+    ("bf16_d1024", True, 2, 8, False)])
 def test_build_is_deterministic(name, packed, R, W, multi_kernel):
     # ten builds of the same inputs, bit for bit (fixed-order reductions, no
     # floating-point atomics)
