@@ -7,11 +7,12 @@ shares no code with the HIP library and never imports it.
 Sources (page title, section):
 
 * "DARTree: Teaching a Chain-Trained Corrector to Think in Trees" (alanhou.org),
-  section "Core Mechanism" and its diagram: at each depth one batched call of
-  the AR correction head over all W surviving paths, top-k children per path,
-  candidates scored by accumulated path probability, keep the top W, repeat for
-  D depths (D head calls); then best-first pruning over the cached scores
-  builds the verification tree and its sparse attention mask.
+  section "Core Mechanism" and its diagram: each depth makes one batched call
+  of the AR correction head over the W live branches, each branch proposes
+  its k best children, the W*k children are ranked by path log-probability
+  and W of them survive, for D depths (so D head calls); best-first pruning
+  over the stored scores then gives the verification tree and its sparse
+  attention mask.
 * "Technische Samenvatting: DARTree" (gist.science), section "Methodologie",
   part 1 "Depth-Wise Parallel AR Expansie": candidates scored by corrected
   cumulative probability, the top-W branches kept and their correction states
