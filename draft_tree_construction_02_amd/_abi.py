@@ -24,7 +24,7 @@ KERNEL_CLASSES = {"gemm1": 0, "gemm2": 1, "head": 2, "merge_select": 3, "reduce"
 # every symbol include/dartree.h declares
 EXPORTS = [
     "dartree_status_string", "dartree_version", "pack_head_bytes", "pack_head",
-    "build_supertree_workspace_size", "build_supertree",
+    "build_supertree_workspace_size", "build_supertree", "build_supertree_noalloc",
     "build_supertree_ex_workspace_size", "build_supertree_ex",
     "head_step_workspace_size", "state_update", "corrected_topk",
     "build_tree_sequential_workspace_size", "build_tree_sequential",
@@ -75,6 +75,8 @@ def lib():
             "build_supertree_workspace_size": (sz, [hp, i32, i32, i32, i32]),
             "build_supertree": (i32, [hp, vp, vp, vp, i32, i32, i32, i32, f32,
                                       vp, vp, vp, vp, vp, sz, vp]),
+            "build_supertree_noalloc": (i32, [hp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                              vp, vp, vp, vp, vp]),
             "build_supertree_ex_workspace_size": (sz, [hp, i32, i32, i32, i32,
                                                        C.POINTER(dt_build_opts)]),
             "build_supertree_ex": (i32, [hp, vp, vp, vp, i32, i32, i32, i32, f32,
@@ -235,6 +237,37 @@ def build_supertree(head: Head, h, s0, root_tok, D: int, W: int, k: int, T: floa
                                   _ptr(out["pool_parent"]), _ptr(out["pool_score"]),
                                   _ptr(out["n_valid"]), _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "build_supertree_ex")
+    return out
+
+
+# the static device scratch of build_supertree_noalloc (DT_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def build_supertree_noalloc(head: Head, h, s0, root_tok, D: int, W: int, k: int, T: float,
+                            out: dict, stream=None) -> dict:
+    """build_supertree without a workspace: the library takes its scratch from
+    a static per-GPU device array, so the call allocates nothing.  The caller
+    passes the outputs (``out``: pool_tok, pool_parent, pool_score, n_valid as
+    build_supertree returns them).  Calls that overlap on one GPU race."""
+    R = s0.shape[0]
+    _dev(h, torch.float32, "h", (R, D, head.d))
+    _dev(s0, torch.float32, "s0", (R, head.d))
+    _dev(root_tok, torch.int32, "root_tok", (R,))
+    _dev(out["pool_tok"], torch.int32, "pool_tok", (R, D, W))
+    _dev(out["pool_parent"], torch.int32, "pool_parent", (R, D, W))
+    _dev(out["pool_score"], torch.float32, "pool_score", (R, D, W))
+    _dev(out["n_valid"], torch.int32, "n_valid", (R, D))
+    rc = lib().build_supertree_noalloc(head.ref, _ptr(h), _ptr(s0), _ptr(root_tok), R, D, W, k,
+                                       float(T), _ptr(out["pool_tok"]), _ptr(out["pool_parent"]),
+                                       _ptr(out["pool_score"]), _ptr(out["n_valid"]),
+                                       _stream(stream))
+    if rc == -3:
+        need = build_supertree_workspace_size(head, R, D, W, k)
+        if need > NOALLOC_SCRATCH_BYTES:
+            raise DartreeError(rc, f"build_supertree_noalloc: needs {need} bytes of scratch, "
+                                   f"the static array holds {NOALLOC_SCRATCH_BYTES}")
+    _check(rc, "build_supertree_noalloc")
     return out
 
 

@@ -960,6 +960,62 @@ int build_tree_mask(const int32_t* sel_parent, const int32_t* n_sel, int R, int 
   return e == hipSuccess ? DT_OK : DT_EHIP;
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free build
+// Device scratch of build_supertree_noalloc: one copy per GPU, held from the
+// first call on that GPU until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device address: kernels and copies
+// take the per-device pointer resolved below.
+static __device__ __align__(256) unsigned char scratch[DT_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+
+// The current device's copy of `scratch`, resolved once per device with that
+// device current.  Returns DT_OK or DT_EHIP / DT_EUNSUPPORTED.
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return DT_EHIP;
+  if (dev >= SCRATCH_MAX_DEVICES) return DT_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DT_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int build_supertree_noalloc(const dt_head* head, const float* h, const float* s0,
+                            const int32_t* root_tok, int R, int D, int W, int k, float T,
+                            int32_t* pool_tok, int32_t* pool_parent, float* pool_score,
+                            int32_t* n_valid, void* stream) {
+  int rc = build_args_ok(head, R, D, W, k);
+  if (rc != DT_OK) return rc;
+  if (!h || !s0 || !root_tok || !pool_tok || !pool_parent || !pool_score || !n_valid)
+    return DT_EINVAL;
+  if (!(T >= 0.f) || !isfinite(T)) return DT_EINVAL;
+  // checked before the scratch is touched, so an oversized call launches nothing
+  const size_t need = build_supertree_workspace_size(head, R, D, W, k);
+  if (need > DT_NOALLOC_SCRATCH_BYTES) return DT_EUNSUPPORTED;
+  void* ws = nullptr;
+  rc = scratch_for_current_device(&ws);
+  if (rc != DT_OK) return rc;
+  // every kernel of the build writes what a later one reads (padding rows
+  // included), so nothing in the scratch has to start at zero
+  return build_supertree_ex(head, h, s0, root_tok, R, D, W, k, T, nullptr, pool_tok, pool_parent,
+                            pool_score, n_valid, ws, DT_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int dartree_timing_enable(int enable) {
   std::lock_guard<std::mutex> lk(g_timing.mu);
   g_timing.on = enable != 0;

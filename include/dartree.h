@@ -168,6 +168,30 @@ int build_supertree(const dt_head* head, const float* h, const float* s0,
                     int32_t* n_valid, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/*
+ * build_supertree_noalloc - build_supertree for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels and the same results, bit for bit,
+ * with the scratch memory taken from a static device array of
+ * DT_NOALLOC_SCRATCH_BYTES inside the library instead of a caller workspace.
+ * Each GPU the library runs on holds its own copy of that array from the
+ * first call on it until the process ends; the call itself allocates and
+ * frees nothing.  The caller still passes every input and output; arguments,
+ * outputs and errors are those of build_supertree, plus DT_EUNSUPPORTED when
+ * build_supertree_workspace_size for these arguments exceeds
+ * DT_NOALLOC_SCRATCH_BYTES (checked on the host; nothing is launched).
+ * The current device must be the one `stream` belongs to.  All calls on one
+ * GPU share its array: calls that overlap in time on one GPU (two streams, two
+ * threads) race and give undefined results.  The array keeps the last call's
+ * contents; no part of it needs to start at zero.
+ */
+#define DT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int build_supertree_noalloc(const dt_head* head, const float* h, const float* s0,
+                            const int32_t* root_tok, int R, int D, int W, int k, float T,
+                            int32_t* pool_tok, int32_t* pool_parent, float* pool_score,
+                            int32_t* n_valid, void* stream);
+
 /* Build variants (dt_build_opts.flags). */
 #define DT_BUILD_MARKOV 1           /* no carried state: every update starts from s0    */
 #define DT_BUILD_BASE_CANDIDATES 2  /* children only among the depth's base candidates   */

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     L = A.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -85,6 +85,39 @@ def seq(hd, D=16, k=8, B=64, beta=0.0, T=1.0, ws=1 << 40, wsp=1, **kw):
     return A.lib().build_tree_sequential(C.byref(hd), p["hid"], p["s0"], p["root"], D, k, B,
                                          beta, T, p["tok"], p["par"], p["depth"], p["score"],
                                          p["n"], wsp, ws, None)
+
+
+def noalloc(hd, R=1, D=16, W=16, k=8, T=1.0, **kw):
+    p = dict(hid=1, s0=1, root=1, tok=1, par=1, score=1, nv=1)
+    p.update(kw)
+    return A.lib().build_supertree_noalloc(C.byref(hd), p["hid"], p["s0"], p["root"], R, D, W,
+                                           k, T, p["tok"], p["par"], p["score"], p["nv"], None)
+
+
+def test_build_supertree_noalloc_validation():
+    # argument checks as build_supertree; a call whose scratch would exceed the
+    # static array is refused on the host before the array is looked up
+    h = fake_head()
+    assert noalloc(h, k=0) == DT_EINVAL
+    assert noalloc(h, T=-1.0) == DT_EINVAL
+    assert noalloc(h, T=float("nan")) == DT_EINVAL
+    assert noalloc(h, tok=None) == DT_EINVAL
+    assert noalloc(h, R=9, W=16) == DT_EUNSUPPORTED          # 144 rows
+    assert noalloc(fake_head(d=100)) == DT_EINVAL
+    big = fake_head(d=8192, V=262144)
+    need = A.lib().build_supertree_workspace_size(C.byref(big), 8, 16, 16, 16)
+    assert need > A.NOALLOC_SCRATCH_BYTES
+    assert noalloc(big, R=8, D=16, W=16, k=16) == DT_EUNSUPPORTED
+    # every benchmarked workload fits the static array
+    from draft_tree_construction_02_amd import synth
+    for wl in synth.workloads().values():
+        hd = fake_head(d=wl.d, V=wl.V, wdtype=A.DT_BF16 if wl.wdtype == "bf16" else A.DT_F32)
+        assert 0 < A.lib().build_supertree_workspace_size(C.byref(hd), wl.R, wl.D, wl.W,
+                                                          wl.k) <= A.NOALLOC_SCRATCH_BYTES
+    # the limit the binding states is the header's
+    text = open(HEADER).read()
+    assert "#define DT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert A.NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
 def test_build_tree_sequential_validation():
