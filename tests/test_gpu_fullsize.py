@@ -1,6 +1,9 @@
-"""Full-size parity: the workloads the benchmark times, in its launch
-configuration (packed bf16 head), checked on sampled teacher-forced paths by
-the fp64 oracle plus size-independent properties of every output."""
+"""Full-size parity: every workload the benchmark times, in its launch
+configuration (packed bf16 head, one call over all requests), checked in full
+by the fp64 oracle - every depth, every row, every survivor, the top-B and
+the mask of every request (``gpu_util.full_check``) - and the full round of
+the Qwen3-8B shape: its pruned 128-node tree verified by one tree-attention
+layer over that tree's own mask."""
 import math
 
 import numpy as np
@@ -11,75 +14,91 @@ from draft_tree_construction_02_amd import _abi as A
 from draft_tree_construction_02_amd import synth
 from oracle import dartree_oracle as O
 from oracle import sampled as S
-from tests.gpu_util import DEV, bf16_dev, dev_requests, dev_weights, oracle_head, to_np, tolerances
+from tests.gpu_util import (DEV, bf16_dev, dev_requests, dev_weights, full_check, oracle_head,
+                            to_np, tolerances)
 
 pytestmark = pytest.mark.gpu
 
-CASES = {
-    "qwen3_4b": 1,          # random sampled nodes per depth per request
-    "qwen3_4b_t0": 0,
-    "qwen3_8b": 1,
-    "qwen3_8b_x8": 0,
-}
+VERIFY = dict(Hq=32, Hkv=8, hd=128, P=4096)      # the Qwen3-8B attention layer shape
+
+_HEAD = {}     # one head at a time: (V, d, wdtype, seed) -> (weights, fp64 oracle head)
+_RUNS = {}     # workload -> (requests, device outputs as numpy)
 
 
-def check_selection(pool_score, pool_parent, n_valid, B, beta, sel, mask):
-    """The device tree is a valid top-B of its pool under prio = score + beta
-    depth (ties by depth, slot), ancestor-closed, emitted in (depth, slot)
-    order, and its mask is the ancestor closure."""
-    D, W = pool_score.shape
-    nodes = [(t, j) for t in range(D) for j in range(int(n_valid[t]))]
-    n = int(sel["n"])
-    assert n == min(B, len(nodes))
-    chosen = [divmod(int(x), W) for x in sel["node"][:n]]
-    assert chosen == sorted(set(chosen))
-    index = {c: i for i, c in enumerate(chosen)}
-    for i, (t, j) in enumerate(chosen):
-        assert int(sel["depth"][i]) == t + 1
-        want = -1 if t == 0 else index[(t - 1, int(pool_parent[t, j]))]
-        assert int(sel["parent"][i]) == want
-    assert np.all(sel["node"][n:] == -1)
-    key = {c: (float(np.float32(pool_score[c]) + np.float32(beta) * np.float32(c[0] + 1)),
-               -c[0], -c[1]) for c in nodes}
-    cset = set(chosen)
-    rest = [key[c] for c in nodes if c not in cset]
-    if rest:
-        assert min(key[c] for c in chosen) > max(rest)
-    assert np.array_equal(mask, O.tree_mask(np.asarray(sel["parent"]), n, B))
+def _head(wl):
+    key = (wl.V, wl.d, wl.wdtype, wl.weight_seed)
+    if key not in _HEAD:
+        _HEAD.clear()
+        hw = synth.make_head(wl.V, wl.d, wl.wdtype, wl.weight_seed)
+        _HEAD[key] = (hw, oracle_head(hw))
+    return _HEAD[key]
 
 
-@pytest.mark.parametrize("name", list(CASES))
-def test_fullsize_build_prune_mask(name):
+def _device_run(name):
+    """build + prune + mask of every request in one call each, as the bench
+    runs them; the Qwen3-8B shape also runs the verification layer over
+    request 0's pruned tree, as the bench's step does."""
+    if name in _RUNS:
+        return _RUNS[name]
     wl = synth.workloads()[name]
-    print(f"full-size case {name}", flush=True)
-    hw, req = synth.make_workload_inputs(wl)
+    hw, _ = _head(wl)
+    req = synth.make_requests(wl.d, wl.D, wl.seeds, wl.h_scale, wl.root_tok)
     head = dev_weights(hw, packed=True)
     h, s0, root = dev_requests(req)
     out = A.build_supertree(head, h, s0, root, wl.D, wl.W, wl.k, wl.T)
     sel = A.prune_topB(out["pool_score"], out["pool_parent"], out["n_valid"], wl.B, wl.beta)
     mask = A.build_tree_mask(sel["sel_parent"], sel["n_sel"])
+    attn = None
+    if name == "qwen3_8b":
+        x = synth.make_verify_inputs(wl.B, VERIFY["P"], VERIFY["Hq"], VERIFY["Hkv"],
+                                     VERIFY["hd"], seed=wl.seeds[0])
+        args = [bf16_dev(x[kk]) for kk in ("q", "k_prefix", "v_prefix", "k_tree", "v_tree")]
+        got = A.tree_attention_verify(*args, mask[0], 1.0 / math.sqrt(VERIFY["hd"]))
+        attn = (x, got.cpu().numpy())
     torch.cuda.synchronize()
-    pool, sel, mask = to_np(out), to_np(sel), mask.cpu().numpy().view(np.uint32)
+    res = (wl, req, to_np(out), to_np(sel), mask.cpu().numpy().view(np.uint32), attn)
     del head
     torch.cuda.empty_cache()
-    tol, tau = tolerances(wl.wdtype)
-    ohead = oracle_head(hw)
-    stats = []
-    for r in range(wl.R):
-        dev = dict(tok=pool["pool_tok"][r], parent=pool["pool_parent"][r],
-                   score=pool["pool_score"][r], n_valid=pool["n_valid"][r])
-        bad = S.check_structure(dev["tok"], dev["parent"], dev["score"], dev["n_valid"], wl.W,
-                                wl.k, wl.V, wl.T)
-        assert not bad, bad
-        check_selection(dev["score"], dev["parent"], dev["n_valid"], wl.B, wl.beta,
-                        dict(node=sel["sel_node"][r], parent=sel["sel_parent"][r],
-                             depth=sel["sel_depth"][r], n=sel["n_sel"][r]), mask[r])
-        paths = S.sample_paths(dev["tok"], dev["parent"], dev["n_valid"], CASES[name], seed=r)
-        fails, st = S.check_paths(ohead, req.h[r], req.s0[r], int(req.root_tok[r]), wl.k, wl.T,
-                                  dev, tol, tau, paths)
-        assert not fails, fails[:5]
-        stats.append(st)
-    print(f"{name}: {stats}", flush=True)
+    _RUNS[name] = res
+    return res
+
+
+CASES = [("qwen3_4b", 0), ("qwen3_4b_t0", 0), ("qwen3_8b", 0)] + \
+        [("qwen3_8b_x8", r) for r in range(8)]
+
+
+@pytest.mark.parametrize("name,r", CASES)
+def test_fullsize_build_prune_mask_full_oracle_check(name, r):
+    print(f"full-size case {name} request {r}", flush=True)
+    wl, req, pool, sel, mask, _ = _device_run(name)
+    _, ohead = _head(wl)
+    assert not S.check_structure(pool["pool_tok"][r], pool["pool_parent"][r],
+                                 pool["pool_score"][r], pool["n_valid"][r], wl.W, wl.k, wl.V, wl.T)
+    st = full_check(ohead, req, r, wl, pool, sel, mask, want_entropy=(name == "qwen3_8b"))
+    print(f"{name}[{r}]: {st}", flush=True)
+    if name == "qwen3_8b":
+        # the workload's inputs are calibrated to a mean entropy of 2 nats
+        assert abs(st["mean_entropy"] - 2.0) <= 0.05, st
+
+
+def test_fullsize_round_with_verification():
+    # the full round of the Qwen3-8B shape: its supertree pruned to B = 128,
+    # then one tree-attention layer (32 query heads, 8 KV heads, head_dim 128,
+    # 4096 prefix tokens) over that tree's own ancestor mask
+    print("full round qwen3_8b: build, prune, mask, verification layer", flush=True)
+    wl, req, pool, sel, mask, (x, got) = _device_run("qwen3_8b")
+    n = int(sel["n_sel"][0])
+    assert n == wl.B == 128
+    assert np.array_equal(mask[0], O.tree_mask(sel["sel_parent"][0], n, wl.B))
+    f = lambda b: synth.bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
+    want = O.tree_attention(f(x["q"]), f(x["k_prefix"]), f(x["v_prefix"]), f(x["k_tree"]),
+                            f(x["v_tree"]), mask[0], n, 1.0 / math.sqrt(VERIFY["hd"]))
+    err = np.max(np.abs(got - want))
+    assert err <= 1e-2 * np.max(np.abs(want)), err
+    assert np.linalg.norm(got - want) <= 1e-2 * np.linalg.norm(want)
+    depth = sel["sel_depth"][0][:n]
+    print(f"round: tree depths {int(depth.min())}..{int(depth.max())}, attention max err "
+          f"{err:.3g} (max |ref| {np.max(np.abs(want)):.3g})", flush=True)
 
 
 def test_fullsize_tree_attention():

@@ -1237,3 +1237,47 @@ def test_check_structure_rejects_planted_mistakes():
     dev["score"][2, 0] = -0.5
     got = S.check_structure(dev["tok"], dev["parent"], dev["score"], dev["n_valid"], W, k, V, 0.0)
     assert any("greedy scores not 0" in m for m in got), got
+
+
+def test_full_check_accepts_the_oracle_and_rejects_a_planted_mistake():
+    # the whole-request check the GPU tests run, fed the oracle's own build,
+    # top-B and mask in the device's storage types ([R][D][W] int32 / float32)
+    from draft_tree_construction_02_amd import synth
+    from tests.gpu_util import full_check, oracle_head
+    wl = synth.Workload("cpu_full_check", V=300, d=128, wdtype="bf16", D=4, W=6, k=3, B=10,
+                        beta=-0.05, T=1.0, R=2, seeds=(5, 6))
+    hw, req = synth.make_workload_inputs(wl)
+    ohead = oracle_head(hw)
+    pool = dict(pool_tok=[], pool_parent=[], pool_score=[], n_valid=[])
+    sel = dict(sel_node=[], sel_parent=[], sel_depth=[], n_sel=[])
+    masks = []
+    for r in range(wl.R):
+        t = O.build_supertree(ohead, req.h[r], req.s0[r], int(req.root_tok[r]), wl.D, wl.W,
+                              wl.k, wl.T)
+        vt = O.prune_topB(t.score, t.parent, t.n_valid, wl.B, wl.beta)
+        pool["pool_tok"].append(t.tok); pool["pool_parent"].append(t.parent)
+        pool["pool_score"].append(t.score); pool["n_valid"].append(t.n_valid)
+
+        def pad(a):
+            o = np.full(wl.B, -1, np.int32)
+            o[:vt.n] = a
+            return o
+        sel["sel_node"].append(pad(vt.node)); sel["sel_parent"].append(pad(vt.parent))
+        sel["sel_depth"].append(pad(vt.depth)); sel["n_sel"].append(vt.n)
+        masks.append(O.tree_mask(vt.parent, vt.n, wl.B))
+    pool = {kk: np.stack(v).astype(np.float32 if kk == "pool_score" else np.int32)
+            for kk, v in pool.items()}
+    sel = {kk: np.array(v, np.int32) for kk, v in sel.items()}
+    mask = np.stack(masks)
+    for r in range(wl.R):
+        st = full_check(ohead, req, r, wl, pool, sel, mask)
+        assert st["exact"] and st["exemptions"] == 0 and st["max_score_err"] < 1e-6
+        assert st["n_sel"] == wl.B
+    bad = mask.copy()
+    bad[1, 4, 0] ^= np.uint32(1)
+    with pytest.raises(AssertionError):
+        full_check(ohead, req, 1, wl, pool, sel, bad)
+    badsel = {kk: v.copy() for kk, v in sel.items()}
+    badsel["sel_parent"][0, 5] = -1 if badsel["sel_parent"][0, 5] >= 0 else 0
+    with pytest.raises(AssertionError):
+        full_check(ohead, req, 0, wl, pool, badsel, mask)
