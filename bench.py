@@ -16,7 +16,11 @@ the timed step: sequential_baseline (one head call per expanded node, same
 budget) and acceptance (tokens per round of the pruned trees, and of the
 sequential tree, under a synthetic greedy target; the walk's own time).
 
-  python bench.py [--steps K] [--warmup W] [--workload qwen3_4b]
+  python bench.py [--steps K] [--warmup W] [--workload qwen3_8b_x8]
+
+The default workload is the largest one that fits one GPU: 8 independent
+Qwen3-8B-shaped requests (d=4096, V=151936, D=16, W=16, k=8, B=96 each)
+sharing one head, so the head streams once per depth for all 128 rows.
 """
 from __future__ import annotations
 
@@ -66,7 +70,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_4b")
+    ap.add_argument("--workload", default="qwen3_8b_x8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sequential", action="store_true",
                     help="skip the sequential best-first (one head call per node) comparison")
@@ -74,8 +78,11 @@ def parse():
                     help="skip the acceptance walk against the synthetic target")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the timing of the step captured in a HIP graph")
-    ap.add_argument("--cpu-builds", type=int, default=1,
-                    help="oracle builds timed for cpu_baseline")
+    ap.add_argument("--cpu-builds", type=int, default=3,
+                    help="oracle builds timed for cpu_baseline (one request per build, "
+                         "cycling over the requests of the batch)")
+    ap.add_argument("--cpu-budget-s", type=float, default=40.0,
+                    help="stop timing further oracle builds once this much CPU time is spent")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for "
                          "hardware byte counters) and exit")
@@ -305,7 +312,8 @@ def main():
     if not args.no_walk:
         res["acceptance"] = acceptance(A, synth, hw, wl, up, h, s0, root, pool, sel, seq_tree)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, hw, req, args.cpu_builds)
+        res["cpu_baseline"] = cpu_baseline(wl, hw, req, max(args.cpu_builds, wl.R),
+                                           args.cpu_budget_s)
     print(json.dumps(res), flush=True)
 
 
@@ -420,31 +428,49 @@ def acceptance(A, synth, hw, wl, up, h, s0, root, pool, sel, seq_tree):
     return res
 
 
-def cpu_baseline(wl, hw, req, nbuilds):
+def cpu_baseline(wl, hw, req, nbuilds, budget_s):
     """The fp64 oracle as it stands, on this host's cores, on a bounded sample:
-    `nbuilds` full builds of request 0 (all D depths) plus prune and mask."""
-    from threadpoolctl import threadpool_info
+    full builds (all D depths) plus prune and mask of the workload's requests,
+    one request per build in order (request r % R), up to `nbuilds` builds or
+    until `budget_s` seconds have been spent; the value is builds per second
+    of oracle time (the median build for a single request)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import dartree_oracle as O
-    t0 = time.time()
-    ohead = O.OracleHead(hw.wdtype, hw.E, hw.W1t, hw.W2t, hw.Ut)
-    prep = time.time() - t0
-    times = []
-    for _ in range(nbuilds):
-        t1 = time.perf_counter()
-        tree = O.build_supertree(ohead, req.h[0], req.s0[0], int(req.root_tok[0]), wl.D, wl.W,
-                                 wl.k, wl.T)
-        vt = O.prune_topB(tree.score, tree.parent, tree.n_valid, wl.B, wl.beta)
-        O.tree_mask(vt.parent, vt.n, wl.B)
-        times.append(time.perf_counter() - t1)
-    info = threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info] or [1])
-    med = sorted(times)[len(times) // 2]
-    log(f"[bench] oracle build {med:.2f}s (weights widened in {prep:.1f}s), {cores} threads")
-    return {"value": round(1.0 / med, 5), "unit": "builds/s", "cores": cores, "kind": "oracle",
-            "sample": f"{nbuilds} full fp64 oracle build(s) of request 0 ({wl.name}: D={wl.D}, "
-                      f"W={wl.W}, k={wl.k}) + prune + mask; median; weight widening "
-                      f"({prep:.1f}s) excluded",
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores, user_api="blas"):
+        t0 = time.time()
+        ohead = O.OracleHead(hw.wdtype, hw.E, hw.W1t, hw.W2t, hw.Ut)
+        prep = time.time() - t0
+        times, done = [], []
+        for i in range(nbuilds):
+            r = i % wl.R
+            t1 = time.perf_counter()
+            tree = O.build_supertree(ohead, req.h[r], req.s0[r], int(req.root_tok[r]), wl.D,
+                                     wl.W, wl.k, wl.T)
+            vt = O.prune_topB(tree.score, tree.parent, tree.n_valid, wl.B, wl.beta)
+            O.tree_mask(vt.parent, vt.n, wl.B)
+            times.append(time.perf_counter() - t1)
+            done.append(r)
+            if sum(times) >= budget_s:
+                break
+        info = threadpool_info()
+    blas_threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"]
+                       or [1])
+    if wl.R > 1:
+        value = len(times) / sum(times)
+        how = (f"{len(times)} full fp64 oracle builds, requests {sorted(set(done))} of "
+               f"{wl.R} ({wl.name}: D={wl.D}, W={wl.W}, k={wl.k}, d={wl.d}), each + prune + "
+               f"mask; builds per second of total oracle time")
+    else:
+        value = 1.0 / sorted(times)[len(times) // 2]
+        how = (f"{len(times)} full fp64 oracle build(s) of request 0 ({wl.name}: D={wl.D}, "
+               f"W={wl.W}, k={wl.k}, d={wl.d}) + prune + mask; median")
+    log(f"[bench] oracle: {len(times)} builds in {sum(times):.1f}s -> {value:.4f} builds/s "
+        f"(weights widened in {prep:.1f}s), {cores} cores, {blas_threads} BLAS threads")
+    return {"value": round(value, 5), "unit": "builds/s", "cores": cores, "kind": "oracle",
+            "sample": how + f"; weight widening ({prep:.1f}s) excluded; budget {budget_s:.0f}s",
+            "seconds": round(sum(times), 2), "blas_threads": blas_threads,
             "blas": ",".join(sorted({i.get('internal_api', '?') for i in info}))}
 
 
