@@ -47,6 +47,7 @@ constexpr int R8_NCMAX = 10;                                    // 32-column til
 constexpr int R8_BLK = 512;                                     // bf16 per 1 KB fragment
 constexpr int R8_ACT = 4;                                       // activation loads per step
 constexpr int R8_PER_CU = 2;                                    // resident workgroups per unit
+constexpr int R8_CAND = 20;                                     // top-k candidates per thread in LDS
 
 constexpr int R8_MAX_DEVICES = 64;
 int g_cus[R8_MAX_DEVICES] = {};
@@ -282,32 +283,108 @@ void k_head_rows128(HeadArgs p) {
                                              p.d / 32, acc, Ws);
   }
 
-  // per-row statistics of the slice: lanes l and l ^ 32 hold the same row
+  // per-row statistics of the slice: lanes l and l ^ 32 hold the same row.
+  // Element e of tile c is column col0 + 32 c + 8 (e / 4) + e % 4; it is
+  // valid when c < T and the column is inside the vocabulary (offset < lim).
+  // The accumulators are scaled by 1/T in place and invalid ones set to -inf.
   const float scale = p.greedy ? 1.f : p.inv_T;
   const int col0 = 32 * tb + 4 * hh;
-  float mx = -INFINITY;
-  TopK<KMAX> tk;
-  tk.clear();
+  const int lim = p.V - col0;
 #pragma unroll
   for (int c = 0; c < R8_NCMAX; ++c)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int col = col0 + 32 * c + 8 * (e >> 2) + (e & 3);
-      const float v = acc[c][e] * scale;
-      if (c < T && col < p.V) {
-        mx = fmaxf(mx, v);
-        tk.insert(make_key(v, (uint32_t)col));
+      const int off = 32 * c + 8 * (e >> 2) + (e & 3);
+      acc[c][e] = (c < T && off < lim) ? acc[c][e] * scale : -INFINITY;
+    }
+  float mx = -INFINITY;
+  TopK<KMAX> tk;
+  tk.clear();
+  bool full = true;           // insert every valid element (the exact rule)
+  if constexpr (KMAX == 4 || KMAX == 8) {
+    // The lane's 160 values in 20 groups of 8 (half a tile each).  tau, the
+    // KMAX-th largest group maximum, is at most the lane's KMAX-th largest
+    // value (KMAX distinct groups hold a value >= tau), so every element of
+    // the top-KMAX, ties at its boundary included, is >= tau.  Only those
+    // candidates (about KMAX + 2 per lane) are written to LDS and inserted;
+    // in wave lockstep the full insertion would run the network for almost
+    // every one of the 160 values.  A lane with more than R8_CAND candidates
+    // (fewer than KMAX valid groups, or many equal values) sends its wave
+    // down the full insertion instead.  Both give the same list.
+    float top[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) top[i] = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < 2 * R8_NCMAX; ++g) {
+      float x = acc[g >> 1][8 * (g & 1)];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) x = fmaxf(x, acc[g >> 1][8 * (g & 1) + i]);
+      mx = fmaxf(mx, x);
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) {
+        const float hi = fmaxf(top[i], x);
+        x = fminf(top[i], x);
+        top[i] = hi;
       }
     }
-  float sum = 0.f;
-  if (!p.greedy) {
+    const float tau = top[KMAX - 1];
+    static_assert(R8_CAND == 20 && 10 * 64 * R8_WAVES * 8 <= C::SLOT * 2,
+                  "two slot arrays hold the candidates");
+    // the slot arrays are free once every wave is past its last K step
+    __syncthreads();
+    uint64_t* cand0 = (uint64_t*)Ws0;                     // candidates 0 .. 9 of each thread
+    uint64_t* cand1 = (uint64_t*)Ws1;                     // candidates 10 .. 19
+    const int tid = threadIdx.x;
+    int cnt = 0;
+    if (tau > -INFINITY) {
+#pragma unroll
+      for (int c = 0; c < R8_NCMAX; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float v = acc[c][e];
+          if (v >= tau) {
+            if (cnt < R8_CAND)
+              (cnt < 10 ? cand0 : cand1)[(cnt < 10 ? cnt : cnt - 10) * 64 * R8_WAVES + tid] =
+                  make_key(v, (uint32_t)(col0 + 32 * c + 8 * (e >> 2) + (e & 3)));
+            ++cnt;
+          }
+        }
+    } else {
+      cnt = R8_CAND + 1;      // fewer than KMAX valid groups
+    }
+    full = __ballot(cnt > R8_CAND) != 0;
+    if (!full) {
+      int n = cnt;
+#pragma unroll
+      for (int m = 1; m < WAVE; m <<= 1) n = max(n, __shfl_xor(n, m, WAVE));
+      n = __builtin_amdgcn_readfirstlane(n);
+      for (int i = 0; i < n; ++i) {
+        uint64_t key = 0;                                   // 0: empty, never kept
+        if (i < cnt) key = (i < 10 ? cand0 : cand1)[(i < 10 ? i : i - 10) * 64 * R8_WAVES + tid];
+        tk.insert(key);
+      }
+    }
+  }
+  if (full) {
 #pragma unroll
     for (int c = 0; c < R8_NCMAX; ++c)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int col = col0 + 32 * c + 8 * (e >> 2) + (e & 3);
-        if (c < T && col < p.V) sum += expf(acc[c][e] * scale - mx);
+        const float v = acc[c][e];
+        if (v > -INFINITY) {
+          mx = fmaxf(mx, v);
+          tk.insert(make_key(v, (uint32_t)(col0 + 32 * c + 8 * (e >> 2) + (e & 3))));
+        }
       }
+  }
+  float sum = 0.f;
+  if (!p.greedy) {
+    // invalid elements add exp(-inf) = 0; a lane without valid elements keeps 0
+    const float m0 = mx > -INFINITY ? mx : 0.f;
+#pragma unroll
+    for (int c = 0; c < R8_NCMAX; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sum += expf(acc[c][e] - m0);
   }
   MaxSum ms{mx, sum};
   {
