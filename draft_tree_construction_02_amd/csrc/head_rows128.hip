@@ -1,30 +1,31 @@
-// Corrected-logit head for 128 rows (many requests sharing one head), gfx950.
+// Corrected-logit head and state-update GEMM for 128 rows (many requests
+// sharing one head), gfx950.
 //
-// Same contract as the other heads (per-row (max, sum exp) and top-k keys of
-// y = s' U / T over each vocabulary slice), shaped for a batch large enough
-// that the matrix cores and the HBM stream have to run at full rate together:
-//   * two workgroups per compute unit, each owning a contiguous slice of
-//     32-column tiles (slices differ by at most one tile), so every unit
-//     streams the same number of bytes and no second round of workgroups
-//     trails behind;
-//   * wave w owns rows 32 w .. 32 w + 31 for all the slice's tiles, so its
-//     accumulators (up to 10 tiles of 32 x 32, all in AGPRs) and its activation
-//     operand (read straight from the packed planes, never shared) are its own,
-//     and the per-row statistics need no exchange between waves;
-//   * the weight tiles of one 32-K step are loaded once per workgroup, each wave
-//     a quarter of them, straight into one of four LDS slots (buffer loads with
-//     the LDS bit) three steps ahead, and all four waves read them from there as
-//     MFMA operands; each wave's activation fragments are requested two steps
-//     ahead, before that step's weights (the vector memory counter completes
-//     in issue order, so waiting for an activation never waits for weights
-//     requested later).  Each slot is its own LDS array, so the compiler can tell a
-//     read of one slot from a load into another and never waits for loads
-//     still in flight to later slots; before each barrier a wave waits (an
-//     explicit count) only for its loads into the next step's slot;
-//   * v_mfma_f32_32x32x16_bf16 with the hi/lo activation split; a slice one
-//     tile short of the maximum runs a loop without the padding tile's MFMAs,
-//     and the longer slices take the lowest workgroup indices so that they
-//     are spread one per unit.
+// The head (k_head_rows128) has the contract of the other heads (per-row
+// (max, sum exp) and top-k keys of y = s' U / T over each vocabulary slice)
+// and is shaped for a batch large enough that the matrix cores and the HBM
+// stream have to run at full rate together:
+//   * one workgroup of 8 waves (two per SIMD) per compute unit, each owning a
+//     contiguous slice of 32-column tiles (slices differ by at most one tile);
+//     wave w takes rows 32 (w % 4) .. + 31 for one half of the slice's tiles,
+//     so its accumulators (up to 10 tiles of 32 x 32) and per-row statistics
+//     are its own, and each half is reported as a slice of its own;
+//   * both operands reach LDS by DMA (buffer loads with the LDS bit): the
+//     weight fragments of one 32-K step (each wave a fifth of them) into one
+//     of three slots two steps ahead, the hi/lo activation blocks of all 128
+//     rows (each wave one row block of each plane) into one of two slots one
+//     step ahead; no register holds data in flight, so the registers the
+//     accumulators leave go to reading operands from LDS well ahead of use,
+//     and the activation is read from L2 once per unit, not once per wave;
+//   * one barrier per K step hands the slots over; it is split-phase: the
+//     next step's activation and first weight fragments are read from LDS
+//     right after it, while the MFMAs of the step's last tiles still run;
+//   * v_mfma_f32_32x32x16_bf16 with the hi/lo activation split; a half of
+//     nine tiles runs a loop without the tenth tile's MFMAs.
+// The GEMM (k_gemm_rows128) keeps the four-wave organisation below
+// (r8_mainloop): wave w owns rows 32 w .. + 31 for all the workgroup's tiles,
+// weight fragments by DMA into four slots three steps ahead, activations
+// straight from the packed planes into registers two steps ahead.
 // Operand layout (both from 16-row x 32-K packed blocks): lane l takes row
 // 16 ((l % 32) / 16) + l % 16 of a 32-row pair of blocks and, in K step st of
 // the block, K values 16 st + 8 (l / 32) .. + 8, i.e. block lane
@@ -32,6 +33,7 @@
 // operands.  Accumulator element e of lane l is vocabulary column
 // 8 (e / 4) + 4 (l / 32) + e % 4 of the tile and row l % 32 of the wave.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -43,11 +45,8 @@ namespace {
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int R8_WAVES = 4;                                     // one per 32-row tile
-constexpr int R8_NCMAX = 10;                                    // 32-column tiles per slice at most
 constexpr int R8_BLK = 512;                                     // bf16 per 1 KB fragment
 constexpr int R8_ACT = 4;                                       // activation loads per step
-constexpr int R8_PER_CU = 2;                                    // resident workgroups per unit
-constexpr int R8_CAND = 20;                                     // top-k candidates per thread in LDS
 
 constexpr int R8_MAX_DEVICES = 64;
 int g_cus[R8_MAX_DEVICES] = {};
@@ -69,15 +68,6 @@ int device_cu_count() {
 namespace {
 
 int cu_count() { return device_cu_count(); }
-
-// Slices of the vocabulary: as many as resident workgroups, each of at most
-// R8_NCMAX tiles and at least 4 (the callers size the partials for slices of
-// 128 columns).
-int r8_slices(int V) {
-  const int nt = (V + 31) / 32;
-  const int need = (nt + R8_NCMAX - 1) / R8_NCMAX;
-  return std::max(std::min((V + 127) / 128, R8_PER_CU * cu_count()), need);
-}
 
 // Fragments per wave per K step and bf16 per LDS slot for NC tiles of 32
 // columns per workgroup.
@@ -251,71 +241,229 @@ __device__ __forceinline__ void r8_mainloop(const uint16_t* W, int nrows_pad, in
   __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
 }
 
-template <int KMAX>
-__global__ __launch_bounds__(64 * R8_WAVES) __attribute__((amdgpu_waves_per_eu(R8_PER_CU, R8_PER_CU)))
-void k_head_rows128(HeadArgs p) {
-  if (p.skip && *p.skip) return;
-  using C = R8Cfg<R8_NCMAX>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ws0[C::SLOT];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws1[C::SLOT];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws2[C::SLOT];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws3[C::SLOT];
+// ---------------------------------------------------------------------------
+// 128-row head (see the file header).
+constexpr int S8_WAVES = 8;
+constexpr int S8_NC = 20;                          // 32-column tiles per slice at most
+constexpr int S8_NCW = S8_NC / 2;                  // tiles per wave (half a slice)
+constexpr int S8_FPW = 2 * S8_NC / S8_WAVES;       // weight fragments per wave per step
+constexpr int S8_WSLOT = 2 * S8_NC * R8_BLK;       // bf16 per weight slot
+constexpr int S8_ASLOT = 16 * R8_BLK;              // bf16 per activation slot
+constexpr int S8_CAND = 20;
+
+// Workgroups of the head: one per compute unit (fewer for a small
+// vocabulary, at least 128 columns each), each slice at most S8_NC tiles.
+int s8_slices(int V) {
+  const int nt = (V + 31) / 32;
+  const int need = (nt + S8_NC - 1) / S8_NC;
+  return std::max(std::min((V + 127) / 128, cu_count()), need);
+}
+
+template <int KMAX, int NCR>
+__device__ __forceinline__ void s8_loop(const HeadArgs& p, int tb, int T, int c0, int nkb,
+                                        f32x16 (&acc)[S8_NCW], uint16_t* const (&Wsl)[3],
+                                        uint16_t* const (&Asl)[2]) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r4 = wave & 3;
+  const int kblocks = p.d / 32, kb_last = nkb - 1;
+  const int hh = lane >> 5, sub = (lane & 31) >> 4;
+  const int vpad = (p.V + PACK_ROWS - 1) / PACK_ROWS * PACK_ROWS;
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.Ut, (short)0, vpad * p.d * 2, 0x00020000);
+  const int w_lane = (sub * R8_BLK + ((lane & 15) + 16 * hh) * 8) * 2;
+  int wsoff[S8_FPW];
+#pragma unroll
+  for (int i = 0; i < S8_FPW; ++i) {
+    const int f = wave + S8_WAVES * i;
+    const int c = min(f / 2, T - 1), st = f % 2;
+    const int j = tb + c;
+    wsoff[i] = __builtin_amdgcn_readfirstlane(
+        (((j / 4) * kblocks * 8 + 2 * (j % 4)) * R8_BLK + 256 * st) * 2);
+  }
+  // activation blocks: wave w copies row block w of the hi and the lo plane
+  const __amdgpu_buffer_rsrc_t hrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.pa.hi, (short)0, 128 * p.d * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t lrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.pa.lo, (short)0, 128 * p.d * 2, 0x00020000);
+  const int a_lane = lane * 16;
+  const int a_soff = __builtin_amdgcn_readfirstlane(wave * kblocks * R8_BLK * 2);
+
+  auto load_w = [&](uint16_t* slot, int kb) {
+    kb = min(kb, kb_last);
+#pragma unroll
+    for (int i = 0; i < S8_FPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wrs, (__attribute__((address_space(3))) void*)(slot + (wave + S8_WAVES * i) * R8_BLK),
+          16, w_lane, wsoff[i] + kb * 8 * R8_BLK * 2, 0, 2 /* nt */);
+  };
+  auto load_a = [&](uint16_t* slot, int kb) {
+    kb = min(kb, kb_last);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        hrs, (__attribute__((address_space(3))) void*)(slot + wave * R8_BLK), 16, a_lane,
+        a_soff + kb * R8_BLK * 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        lrs, (__attribute__((address_space(3))) void*)(slot + (8 + wave) * R8_BLK), 16, a_lane,
+        a_soff + kb * R8_BLK * 2, 0, 0);
+  };
+  constexpr int WAITCNT = (S8_FPW & 15) | ((S8_FPW >> 4) << 14) | (7 << 4) | (15 << 8);
+#pragma unroll
+  for (int c = 0; c < S8_NCW; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+  // prologue: W(0), A(0), W(1); W(0) and A(0) complete before the first barrier
+  load_w(Wsl[0], 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_a(Asl[0], 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(Wsl[1], 1);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(WAITCNT);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  const int a_rd = ((2 * r4 + sub) * R8_BLK + ((lane & 15) + 16 * hh) * 8);   // + plane * 8 blocks + st * 256
+  const int b_rd = 2 * c0 * R8_BLK + lane * 8;
+  static_assert(NCR >= 5 && NCR <= 10, "two groups of tiles per half step");
+  // Split-phase step: the barrier that hands over the next step's slots sits
+  // before the MFMAs of tiles 4 .. NCR - 1 of the second K half, so the next
+  // step's activation fragments and first weight fragments are read from LDS
+  // while those MFMAs run (no LDS latency at the start of a step).
+  struct Carry { bf16x8 a[4]; bf16x8 b[4]; };       // a: (st, hi/lo); b: st 0, tiles 0..3
+  auto rd = [&](const uint16_t* p) { return __builtin_bit_cast(bf16x8, *(const u32x4*)p); };
+  auto read_head = [&](const uint16_t* as, const uint16_t* ws, Carry& c) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      c.a[2 * st] = rd(as + 256 * st);
+      c.a[2 * st + 1] = rd(as + 8 * R8_BLK + 256 * st);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c.b[q] = rd(ws + (2 * q) * R8_BLK);
+  };
+  auto mfma2 = [&](int t, const bf16x8& w, const bf16x8& ahi, const bf16x8& alo) {
+    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, ahi, acc[t], 0, 0, 0);
+    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, alo, acc[t], 0, 0, 0);
+  };
+  Carry cur;
+  read_head(Asl[0] + a_rd, Wsl[0] + b_rd, cur);
+  // scheduling groups: DS reads (0x100) and MFMAs (0x008) in the order written
+#define S8_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+  auto step = [&](auto sw, auto sa, int kb) {
+    constexpr int SW = decltype(sw)::value, SA = decltype(sa)::value;
+    load_a(Asl[(SA + 1) % 2], kb + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(Wsl[(SW + 2) % 3], kb + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* ws = Wsl[SW] + b_rd;
+    constexpr int N0 = NCR - 4;
+    bf16x8 w0[N0], w1[NCR];
+#pragma unroll
+    for (int q = 0; q < N0; ++q) w0[q] = rd(ws + (2 * (4 + q)) * R8_BLK);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mfma2(q, cur.b[q], cur.a[0], cur.a[1]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w1[q] = rd(ws + (2 * q + 1) * R8_BLK);
+#pragma unroll
+    for (int q = 0; q < N0; ++q) mfma2(4 + q, w0[q], cur.a[0], cur.a[1]);
+#pragma unroll
+    for (int q = 4; q < NCR; ++q) w1[q] = rd(ws + (2 * q + 1) * R8_BLK);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mfma2(q, w1[q], cur.a[2], cur.a[3]);
+    S8_GROUP(0x100, N0);
+    S8_GROUP(0x008, 8);
+    S8_GROUP(0x100, 4);
+    S8_GROUP(0x008, 2 * N0);
+    S8_GROUP(0x100, N0);
+    S8_GROUP(0x008, 8);
+    // every read of this step's slots is done (its data is in registers);
+    // own loads of A(kb + 1) and W(kb + 1) complete; then hand over
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(WAITCNT & ~(15 << 8));     // vmcnt(FPW), lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8 ahi = cur.a[2], alo = cur.a[3];
+    read_head(Asl[(SA + 1) % 2] + a_rd, Wsl[(SW + 1) % 3] + b_rd, cur);
+#pragma unroll
+    for (int q = 4; q < NCR; ++q) mfma2(q, w1[q], ahi, alo);
+    S8_GROUP(0x100, 8);
+    S8_GROUP(0x008, 2 * N0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#undef S8_GROUP
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  int kb = 0;
+  for (; kb + 6 <= nkb; kb += 6) {
+    step(I0{}, I0{}, kb);
+    step(I1{}, I1{}, kb + 1);
+    step(I2{}, I0{}, kb + 2);
+    step(I0{}, I1{}, kb + 3);
+    step(I1{}, I0{}, kb + 4);
+    step(I2{}, I1{}, kb + 5);
+  }
+  if (kb < nkb) {            // nkb % 6 is 2 or 4
+    step(I0{}, I0{}, kb);
+    step(I1{}, I1{}, kb + 1);
+    if (kb + 2 < nkb) {
+      step(I2{}, I0{}, kb + 2);
+      step(I0{}, I1{}, kb + 3);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(64 * S8_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_head_rows128(HeadArgs p) {
+  if (p.skip && *p.skip) return;
+  __shared__ __attribute__((aligned(16))) uint16_t W0[S8_WSLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t W1[S8_WSLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t W2[S8_WSLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t A0[S8_ASLOT];
+  __shared__ __attribute__((aligned(16))) uint16_t A1[S8_ASLOT];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r4 = wave & 3, hf = wave >> 2;
   const int G = gridDim.x, slice = blockIdx.x;
   const int nt = (p.V + 31) / 32;
-  // slices one tile longer come first, so that they are the first workgroups
-  // placed on the units (dispatched first, they spread over distinct units)
   const int base = nt / G, extra = nt % G;
   const int tb = slice * base + min(slice, extra);
-  const int T = base + (slice < extra ? 1 : 0);                   // 1 .. R8_NCMAX
+  const int T = base + (slice < extra ? 1 : 0);                   // 1 .. S8_NC
+  const int T0 = (T + 1) / 2;
+  const int c0 = hf ? T0 : 0, Tw = hf ? T - T0 : T0;            // this wave's tiles
   const int hh = lane >> 5;
-  const int vpad = (p.V + PACK_ROWS - 1) / PACK_ROWS * PACK_ROWS;
-  f32x16 acc[R8_NCMAX];
-  uint16_t* const Ws[4] = {Ws0, Ws1, Ws2, Ws3};
-  if (T == R8_NCMAX - 1) {
-    // one tile short of the maximum: its MFMAs are not run (the loads, and so
-    // the LDS layout and the wait counts, stay those of R8_NCMAX tiles)
-    r8_mainloop<R8_NCMAX, R8_NCMAX - 1, KMAX, 4>((const uint16_t*)p.Ut, vpad, p.d, p.pa, tb, T,
-                                                 0, p.d / 32, acc, Ws);
-  } else {
-    r8_mainloop<R8_NCMAX, R8_NCMAX, KMAX, 4>((const uint16_t*)p.Ut, vpad, p.d, p.pa, tb, T, 0,
-                                             p.d / 32, acc, Ws);
-  }
+  f32x16 acc[S8_NCW];
+  uint16_t* const Wsl[3] = {W0, W1, W2};
+  uint16_t* const Asl[2] = {A0, A1};
+  if (Tw == S8_NCW)
+    s8_loop<KMAX, S8_NCW>(p, tb, T, c0, p.d / 32, acc, Wsl, Asl);
+  else
+    s8_loop<KMAX, S8_NCW - 1>(p, tb, T, c0, p.d / 32, acc, Wsl, Asl);
 
-  // per-row statistics of the slice: lanes l and l ^ 32 hold the same row.
-  // Element e of tile c is column col0 + 32 c + 8 (e / 4) + e % 4; it is
-  // valid when c < T and the column is inside the vocabulary (offset < lim).
-  // The accumulators are scaled by 1/T in place and invalid ones set to -inf.
   const float scale = p.greedy ? 1.f : p.inv_T;
-  const int col0 = 32 * tb + 4 * hh;
+  const int col0 = 32 * (tb + c0) + 4 * hh;
   const int lim = p.V - col0;
 #pragma unroll
-  for (int c = 0; c < R8_NCMAX; ++c)
+  for (int c = 0; c < S8_NCW; ++c)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int off = 32 * c + 8 * (e >> 2) + (e & 3);
-      acc[c][e] = (c < T && off < lim) ? acc[c][e] * scale : -INFINITY;
+      acc[c][e] = (c < Tw && off < lim) ? acc[c][e] * scale : -INFINITY;
     }
   float mx = -INFINITY;
   TopK<KMAX> tk;
   tk.clear();
-  bool full = true;           // insert every valid element (the exact rule)
+  bool full = true;
+  __syncthreads();
   if constexpr (KMAX == 4 || KMAX == 8) {
-    // The lane's 160 values in 20 groups of 8 (half a tile each).  tau, the
-    // KMAX-th largest group maximum, is at most the lane's KMAX-th largest
-    // value (KMAX distinct groups hold a value >= tau), so every element of
-    // the top-KMAX, ties at its boundary included, is >= tau.  Only those
-    // candidates (about KMAX + 2 per lane) are written to LDS and inserted;
-    // in wave lockstep the full insertion would run the network for almost
-    // every one of the 160 values.  A lane with more than R8_CAND candidates
-    // (fewer than KMAX valid groups, or many equal values) sends its wave
-    // down the full insertion instead.  Both give the same list.
     float top[KMAX];
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) top[i] = -INFINITY;
 #pragma unroll
-    for (int g = 0; g < 2 * R8_NCMAX; ++g) {
+    for (int g = 0; g < 2 * S8_NCW; ++g) {
       float x = acc[g >> 1][8 * (g & 1)];
 #pragma unroll
       for (int i = 1; i < 8; ++i) x = fmaxf(x, acc[g >> 1][8 * (g & 1) + i]);
@@ -328,46 +476,43 @@ void k_head_rows128(HeadArgs p) {
       }
     }
     const float tau = top[KMAX - 1];
-    static_assert(R8_CAND == 20 && 10 * 64 * R8_WAVES * 8 <= C::SLOT * 2,
-                  "two slot arrays hold the candidates");
-    // the slot arrays are free once every wave is past its last K step
-    __syncthreads();
-    uint64_t* cand0 = (uint64_t*)Ws0;                     // candidates 0 .. 9 of each thread
-    uint64_t* cand1 = (uint64_t*)Ws1;                     // candidates 10 .. 19
+    static_assert(S8_CAND == 20 && 10 * 64 * S8_WAVES * 8 <= S8_WSLOT * 2, "candidate space");
+    uint64_t* cand0 = (uint64_t*)W0;
+    uint64_t* cand1 = (uint64_t*)W1;
     const int tid = threadIdx.x;
     int cnt = 0;
     if (tau > -INFINITY) {
 #pragma unroll
-      for (int c = 0; c < R8_NCMAX; ++c)
+      for (int c = 0; c < S8_NCW; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float v = acc[c][e];
           if (v >= tau) {
-            if (cnt < R8_CAND)
-              (cnt < 10 ? cand0 : cand1)[(cnt < 10 ? cnt : cnt - 10) * 64 * R8_WAVES + tid] =
+            if (cnt < S8_CAND)
+              (cnt < 10 ? cand0 : cand1)[(cnt < 10 ? cnt : cnt - 10) * 64 * S8_WAVES + tid] =
                   make_key(v, (uint32_t)(col0 + 32 * c + 8 * (e >> 2) + (e & 3)));
             ++cnt;
           }
         }
     } else {
-      cnt = R8_CAND + 1;      // fewer than KMAX valid groups
+      cnt = S8_CAND + 1;
     }
-    full = __ballot(cnt > R8_CAND) != 0;
+    full = __ballot(cnt > S8_CAND) != 0;
     if (!full) {
       int n = cnt;
 #pragma unroll
       for (int m = 1; m < WAVE; m <<= 1) n = max(n, __shfl_xor(n, m, WAVE));
       n = __builtin_amdgcn_readfirstlane(n);
       for (int i = 0; i < n; ++i) {
-        uint64_t key = 0;                                   // 0: empty, never kept
-        if (i < cnt) key = (i < 10 ? cand0 : cand1)[(i < 10 ? i : i - 10) * 64 * R8_WAVES + tid];
+        uint64_t key = 0;
+        if (i < cnt) key = (i < 10 ? cand0 : cand1)[(i < 10 ? i : i - 10) * 64 * S8_WAVES + tid];
         tk.insert(key);
       }
     }
   }
   if (full) {
 #pragma unroll
-    for (int c = 0; c < R8_NCMAX; ++c)
+    for (int c = 0; c < S8_NCW; ++c)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const float v = acc[c][e];
@@ -379,10 +524,9 @@ void k_head_rows128(HeadArgs p) {
   }
   float sum = 0.f;
   if (!p.greedy) {
-    // invalid elements add exp(-inf) = 0; a lane without valid elements keeps 0
     const float m0 = mx > -INFINITY ? mx : 0.f;
 #pragma unroll
-    for (int c = 0; c < R8_NCMAX; ++c)
+    for (int c = 0; c < S8_NCW; ++c)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sum += expf(acc[c][e] - m0);
   }
@@ -397,7 +541,8 @@ void k_head_rows128(HeadArgs p) {
     tk.merge(o);
   }
   if (lane < 32) {
-    const long o = (long)(32 * wave + lane) * G + slice;
+    // the two halves of a slice are reported as two consecutive slices
+    const long o = (long)(32 * r4 + lane) * (2 * G) + 2 * slice + hf;
     p.ms_part[o] = make_float2(ms.m, ms.s);
 #pragma unroll
     for (int i = 0; i < KMAX; ++i)
@@ -456,7 +601,7 @@ bool head_rows128_ok(const HeadArgs& p) {
          vpad * p.d * 2 < (1L << 31);
 }
 
-int head_rows128_slices(const HeadArgs& p) { return r8_slices(p.V); }
+int head_rows128_slices(const HeadArgs& p) { return 2 * s8_slices(p.V); }
 
 bool gemm_rows128_ok(const GemmArgs& g) {
   const long npad = (long)(g.N + PACK_ROWS - 1) / PACK_ROWS * PACK_ROWS;
@@ -473,12 +618,12 @@ hipError_t launch_gemm_rows128(const GemmArgs& g, hipStream_t st) {
 }
 
 hipError_t launch_head_rows128(const HeadArgs& p, hipStream_t st) {
-  const dim3 grid(r8_slices(p.V));
+  const dim3 grid(s8_slices(p.V));
   switch (p.kmax) {
-    case 1: hipLaunchKernelGGL(k_head_rows128<1>, grid, dim3(64 * R8_WAVES), 0, st, p); break;
-    case 4: hipLaunchKernelGGL(k_head_rows128<4>, grid, dim3(64 * R8_WAVES), 0, st, p); break;
-    case 8: hipLaunchKernelGGL(k_head_rows128<8>, grid, dim3(64 * R8_WAVES), 0, st, p); break;
-    case 16: hipLaunchKernelGGL(k_head_rows128<16>, grid, dim3(64 * R8_WAVES), 0, st, p); break;
+    case 1: hipLaunchKernelGGL(k_head_rows128<1>, grid, dim3(64 * S8_WAVES), 0, st, p); break;
+    case 4: hipLaunchKernelGGL(k_head_rows128<4>, grid, dim3(64 * S8_WAVES), 0, st, p); break;
+    case 8: hipLaunchKernelGGL(k_head_rows128<8>, grid, dim3(64 * S8_WAVES), 0, st, p); break;
+    case 16: hipLaunchKernelGGL(k_head_rows128<16>, grid, dim3(64 * S8_WAVES), 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
