@@ -13,6 +13,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -169,7 +170,7 @@ StepWs carve_step(Carver& c, const dt_head* h, int rows, int k) {
 // ---------------------------------------------------------------- timing
 struct Timing {
   std::mutex mu;
-  bool on = false;
+  std::atomic<bool> on{false};     // read without the lock on every launch
   std::vector<hipEvent_t> free_ev;
   struct Rec { int cls; hipEvent_t a, b; };
   std::vector<Rec> pending;
@@ -191,7 +192,7 @@ hipEvent_t take_event() {
 // Runs `launch` bracketed by events when timing is on.
 template <class F>
 hipError_t timed(int cls, hipStream_t st, F&& launch) {
-  if (!g_timing.on) return launch();
+  if (!g_timing.on.load(std::memory_order_relaxed)) return launch();
   std::lock_guard<std::mutex> lk(g_timing.mu);
   hipEvent_t a = take_event(), b = take_event();
   if (!a || !b) return launch();
@@ -1018,7 +1019,7 @@ int build_supertree_noalloc(const dt_head* head, const float* h, const float* s0
 
 int dartree_timing_enable(int enable) {
   std::lock_guard<std::mutex> lk(g_timing.mu);
-  g_timing.on = enable != 0;
+  g_timing.on.store(enable != 0);
   return DT_OK;
 }
 

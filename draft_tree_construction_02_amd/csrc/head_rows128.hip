@@ -33,6 +33,7 @@
 // operands.  Accumulator element e of lane l is vocabulary column
 // 8 (e / 4) + 4 (l / 32) + e % 4 of the tile and row l % 32 of the wave.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -49,19 +50,22 @@ constexpr int R8_BLK = 512;                                     // bf16 per 1 KB
 constexpr int R8_ACT = 4;                                       // activation loads per step
 
 constexpr int R8_MAX_DEVICES = 64;
-int g_cus[R8_MAX_DEVICES] = {};
+std::atomic<int> g_cus[R8_MAX_DEVICES];     // 0 until queried
 
 }  // namespace
 
-// Compute units of the current device, queried once per device (a stale
-// read by a concurrent first caller only repeats the query).
+// Compute units of the current device, queried once per device and cached in
+// an atomic (two first callers may both query; they store the same value).
 int device_cu_count() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < R8_MAX_DEVICES && g_cus[dev] > 0) return g_cus[dev];
+  if (dev < R8_MAX_DEVICES) {
+    const int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     return 256;
-  if (dev < R8_MAX_DEVICES) g_cus[dev] = n;
+  if (dev < R8_MAX_DEVICES) g_cus[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 

@@ -22,9 +22,19 @@
  *  - Arguments are validated on the host before anything is launched.  On an
  *    error the call returns a negative dt_status, launches nothing and writes
  *    no output.  Launch failures reported by HIP return DT_EHIP.
- *  - Results are bitwise reproducible for identical inputs: reductions run in
- *    a fixed order and no floating-point atomics are used.
+ *  - Results are bitwise reproducible for identical inputs on a device with
+ *    the same number of compute units: reductions run in a fixed order and no
+ *    floating-point atomics are used, but the launch grids (vocabulary
+ *    slices, split-K counts) are sized from the compute-unit count, so the
+ *    fp32 summation order, and with it the last bits of a score, can differ
+ *    between devices with different counts.
  *  - Calls that share one workspace must not overlap in time.
+ *  - Global state: the library keeps only (a) a per-device cache of the
+ *    compute-unit count (atomic, filled on first use), (b) the kernel timing
+ *    registry of dartree_timing_* (mutex-protected; off by default) and (c)
+ *    the per-device address of build_supertree_noalloc's static scratch
+ *    (mutex-protected, resolved on first use).  Everything else lives in the
+ *    caller's buffers.
  *  - Row-major layouts throughout; "[A][B]" means B is the fastest index.
  */
 #ifndef DARTREE_H
