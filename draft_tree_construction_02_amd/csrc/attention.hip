@@ -5,13 +5,16 @@
 // workgroup (4 waves x 16 rows) owns one key/value head, 64 rows and one
 // contiguous range of keys, where keys [0, P) are the prefix (always visible)
 // and keys [P, P + n) are the tree nodes (visible where the query's ancestor
-// bitmask has the bit).  Keys are processed in blocks of 64 in one pass with
-// an online softmax: the next block's K and V are loaded into registers while
-// the current block, staged in LDS (K row-major, V transposed), feeds
-// S^T = K Q^T and O += P V on v_mfma_f32_16x16x32_bf16 with fp32
-// accumulation; per row the running maximum m and sum l are rescaled when m
-// grows, and P is rounded to bf16 for the PV product.  A combine kernel
-// merges the key ranges: out = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s.
+// bitmask has the bit).  Keys are processed in blocks of 64 in one pass: the
+// next block's K and V are loaded into registers while the current block,
+// staged in LDS (K row-major, V transposed), feeds S^T = K Q^T and
+// O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  In
+// that orientation a lane's O values all belong to its own query row, so the
+// softmax needs no exchange between lanes except when a row's reference
+// maximum moves (see the block body).  Scores are in log2 units and
+// exponentiated with exp2; P is rounded to bf16 for the PV product.  A
+// combine kernel merges the key ranges:
+//   out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 #include <cmath>
 #include <type_traits>
 
@@ -135,7 +138,12 @@ __global__ __launch_bounds__(AT_THREADS) void k_tree_attn(AttnArgs a) {
   }
   const uint32_t* mrow = Ms + (wave * 16 + r16) * (DT_MAX_B / 32);
 
+  // Scores are kept in log2 units (s * scale * log2 e), so the softmax is
+  // exp2 of the shifted score; m, the running maximum, is in the same units.
+  const float sl2 = a.scale * 1.4426950408889634f;
   float m = -INFINITY, l = 0.f;
+  // O^T = V^T P^T: o[t][i] = O(row r16, dim 16 t + 4 g4 + i), so a lane holds
+  // only its own row and the per-row rescale needs no exchange between lanes
   f32x4 o[HD / 16];
 #pragma unroll
   for (int t = 0; t < HD / 16; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -143,6 +151,7 @@ __global__ __launch_bounds__(AT_THREADS) void k_tree_attn(AttnArgs a) {
   u32x4 kv[2][AT_CH], vv[2][AT_CH];
   load_kv(a, g, kbeg, kend, kv[0], vv[0]);
   load_kv(a, g, kbeg + AT_KB, kend, kv[1], vv[1]);
+  const int plain_end = min(a.P, kend);     // keys below this need no mask
   auto block = [&](int kb, auto set_tag) {
     constexpr int SET = decltype(set_tag)::value;
     __syncthreads();                       // every wave is done with the previous tiles
@@ -151,8 +160,8 @@ __global__ __launch_bounds__(AT_THREADS) void k_tree_attn(AttnArgs a) {
     __syncthreads();
     load_kv(a, g, kb + 2 * AT_KB, kend, kv[SET], vv[SET]);
 
-    // S^T: st[h][r] = s(key = kb + 16 h + 4 g4 + r, row = lane % 16), scaled;
-    // masked or missing keys are -inf
+    // S^T: st[h][r] = s(key = kb + 16 h + 4 g4 + r, row = lane % 16), in
+    // log2 units; masked or missing keys are -inf
     float st[4][4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -165,61 +174,86 @@ __global__ __launch_bounds__(AT_THREADS) void k_tree_attn(AttnArgs a) {
                                                       0, 0, 0);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kb + 16 * h + 4 * g4 + r;
-        bool vis = row_ok && key < kend;
-        if (vis && key >= a.P) {
-          const int j = key - a.P;
-          vis = (mrow[j >> 5] >> (j & 31)) & 1u;
+      for (int r = 0; r < 4; ++r) st[h][r] = acc[r] * sl2;
+    }
+    if (!(kb + AT_KB <= plain_end)) {      // wave-uniform: prefix blocks skip the mask
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kb + 16 * h + 4 * g4 + r;
+          bool vis = key < kend;
+          if (vis && key >= a.P) {
+            const int j = key - a.P;
+            vis = (mrow[j >> 5] >> (j & 31)) & 1u;
+          }
+          if (!vis) st[h][r] = -INFINITY;
         }
-        st[h][r] = vis ? acc[r] * a.scale : -INFINITY;
-      }
     }
-    // online softmax: block maximum of the row, rescale l and O
-    float bm = -INFINITY;
+    if (!row_ok) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[h][r] = -INFINITY;
+    }
+    // online softmax against a per-row reference m (not the running maximum):
+    // p = exp2(s - m) is exact for any reference (O and l share it, and the
+    // combine rescales by 2^(m - M)), so O is rescaled only when a score
+    // exceeds m by more than RESCALE, which keeps p <= 2^RESCALE; the decision
+    // is wave-uniform, and in the common case the block needs no exchange
+    // between lanes.  l is summed per lane and reduced across the row's four
+    // lane groups once, at the end.
+    constexpr float RESCALE = 16.f;
+    float lm = -INFINITY;
 #pragma unroll
     for (int h = 0; h < 4; ++h)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) bm = fmaxf(bm, st[h][r]);
-    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-    const float mn = fmaxf(m, bm);
-    const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
-    uint32_t pk[8];
-    float ls = 0.f;
+      for (int r = 0; r < 4; ++r) lm = fmaxf(lm, st[h][r]);
+    if (__ballot(lm > m + RESCALE) != 0) {
+      float bm = fmaxf(lm, __shfl_xor(lm, 16, 64));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      if (bm > m + RESCALE) {                 // this row takes a new reference
+        const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - bm);
+        l *= alpha;
+#pragma unroll
+        for (int t = 0; t < HD / 16; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[t][i] *= alpha;
+        m = bm;
+      }
+    }
+    const float msub = m == -INFINITY ? 0.f : m;     // no visible key yet: p = 0
+    float p[4][4];
 #pragma unroll
     for (int h = 0; h < 4; ++h)
 #pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const float p0 = st[h][r] == -INFINITY ? 0.f : expf(st[h][r] - mn);
-        const float p1 = st[h][r + 1] == -INFINITY ? 0.f : expf(st[h][r + 1] - mn);
-        ls += p0 + p1;
-        pk[h * 2 + r / 2] = f32_to_bf16(p0) | (f32_to_bf16(p1) << 16);
+      for (int r = 0; r < 4; ++r) {
+        p[h][r] = __builtin_amdgcn_exp2f(st[h][r] - msub);     // exp2(-inf) = 0
+        l += p[h][r];
       }
-    ls += __shfl_xor(ls, 16, 64);
-    ls += __shfl_xor(ls, 32, 64);
-    l = l * alpha + ls;
-    m = mn;
-    // O rows of this lane are 4 g4 + r: their factors live in lanes 4 g4 + r
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float ar = __shfl(alpha, 4 * g4 + r, 64);
-#pragma unroll
-      for (int t = 0; t < HD / 16; ++t) o[t][r] *= ar;
-    }
-    // P as the A operand, 32 keys per MFMA: k index 8 g4 + e <-> key
-    // 32 q + 4 g4 + e (e < 4) and 32 q + 16 + 4 g4 + e - 4 (e >= 4)
+    // O^T += V^T P^T, 32 keys per MFMA.  k index 8 g4 + e of lane group g4
+    // <-> key 32 q + 4 g4 + e (e < 4) and 32 q + 16 + 4 g4 + e - 4 (e >= 4):
+    // the B operand (P^T) is then this lane's own p[2 q][.], p[2 q + 1][.],
+    // rounded to bf16, and the A operand (V^T) two 8-byte pieces of a V^T row
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) {
-      const bf16x8 pa = __builtin_bit_cast(
-          bf16x8, u32x4{pk[4 * qq], pk[4 * qq + 1], pk[4 * qq + 2], pk[4 * qq + 3]});
+      typedef __attribute__((ext_vector_type(2))) float f2;
+      typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int h = 2 * qq + e / 2, r = 2 * (e % 2);
+        pk[e] = __builtin_bit_cast(uint32_t,
+                                   __builtin_convertvector(f2{p[h][r], p[h][r + 1]}, b2));
+      }
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
 #pragma unroll
       for (int t = 0; t < HD / 16; ++t) {
         const int dim = 16 * t + r16;
         const uint2 v0 = *(const uint2*)(Vts + dim * VLD + 32 * qq + 4 * g4);
         const uint2 v1 = *(const uint2*)(Vts + dim * VLD + 32 * qq + 16 + 4 * g4);
-        const bf16x8 vb = __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
-        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t], 0, 0, 0);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{v0.x, v0.y, v1.x, v1.y});
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[t], 0, 0, 0);
       }
     }
   };
@@ -230,40 +264,45 @@ __global__ __launch_bounds__(AT_THREADS) void k_tree_attn(AttnArgs a) {
     block(kb + AT_KB, std::integral_constant<int, 1>{});
   }
 
-  // O lane layout: row 4 g4 + r of the wave, dim 16 t + r16
+  // the row's sum over its four lane groups (all hold the same reference m)
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  // this lane's row, dims 16 t + 4 g4 .. + 3
   const long base = ((long)split * a.Hkv + g) * nrows;
+  if (row_ok) {
 #pragma unroll
-  for (int t = 0; t < HD / 16; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int orow = rb * AT_ROWS + wave * 16 + 4 * g4 + r;
-      if (orow < nrows) a.opart[(base + orow) * HD + 16 * t + r16] = o[t][r];
-    }
-  if (row_ok && g4 == 0) a.mlpart[base + row] = make_float2(m, l);
+    for (int t = 0; t < HD / 16; ++t)
+      *(f32x4*)(a.opart + (base + row) * HD + 16 * t + 4 * g4) = o[t];
+    if (g4 == 0) a.mlpart[base + row] = make_float2(m, l);
+  }
 }
 
-// out[i][h][:] for row (i, hh) of key/value head g = h / group.
+// out[i][h][4 j .. 4 j + 3] for row (i, hh) of key/value head g = h / group:
+// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s (m in log2 units).
 __global__ void k_tree_attn_combine(AttnArgs a, float* __restrict__ out) {
   const int nrows = a.n * a.group;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (long)a.Hkv * nrows * HD) return;
-  const int dim = gid % HD;
-  const int row = (gid / HD) % nrows;
-  const int g = gid / ((long)HD * nrows);
+  if (gid >= (long)a.Hkv * nrows * (HD / 4)) return;
+  const int d4 = gid % (HD / 4);
+  const int row = (gid / (HD / 4)) % nrows;
+  const int g = gid / ((long)(HD / 4) * nrows);
   float M = -INFINITY;
   for (int s = 0; s < a.nsplit; ++s)
     M = fmaxf(M, a.mlpart[((long)s * a.Hkv + g) * nrows + row].x);
-  float num = 0.f, den = 0.f;
+  f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
   if (M != -INFINITY)
     for (int s = 0; s < a.nsplit; ++s) {
       const long b = ((long)s * a.Hkv + g) * nrows + row;
       const float2 ml = a.mlpart[b];
-      const float w = ml.x == -INFINITY ? 0.f : expf(ml.x - M);
-      num += w * a.opart[b * HD + dim];
+      const float w = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+      const f32x4 v = *(const f32x4*)(a.opart + b * HD + 4 * d4);
+      num += w * v;
       den += w * ml.y;
     }
   const int i = row / a.group, h = g * a.group + row % a.group;
-  out[((long)i * a.Hq + h) * HD + dim] = den > 0.f ? num / den : 0.f;
+  *(f32x4*)(out + ((long)i * a.Hq + h) * HD + 4 * d4) =
+      den > 0.f ? num / den : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // Key ranges: about DT_ATTN_WGS workgroups (several per CU, so waves hide each
@@ -340,7 +379,7 @@ extern "C" int tree_attention_verify(const void* q, const void* k_prefix, const 
                        c.st, c.a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long tot = (long)c.a.Hkv * c.a.n * c.a.group * HD;
+    const long tot = (long)c.a.Hkv * c.a.n * c.a.group * (HD / 4);
     hipLaunchKernelGGL(k_tree_attn_combine, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0,
                        c.st, c.a, c.out);
     return hipGetLastError();
