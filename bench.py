@@ -260,7 +260,8 @@ def main():
     elif rows_p == 64:
         head_kernel = "k_head_wide (64 columns per wave, 64 rows)"
     else:
-        head_kernel = "k_head_rows128 (one vocabulary slice per workgroup, 32x32x16 MFMA)"
+        head_kernel = ("k_head_rows128 (one 8-wave workgroup per compute unit, operands by LDS DMA, "
+                       "32x32x16 MFMA)")
 
     # weights streamed per step: U (d V) + W1 and W2 (8 d^2) per depth, shared by R requests
     bytes_per_step = D * wbytes * (wl.d * wl.V + 8 * wl.d * wl.d)
