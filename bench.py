@@ -207,17 +207,22 @@ def main():
     # the full steps again with every library launch bracketed by HIP events
     pk_ms, _, _ = timed_region(step, True)
     kern = {}
-    for name in ("gemm1", "gemm2", "reduce", "head", "merge_select", "attention", "build_small"):
+    for name in ("gemm1", "gemm2", "reduce", "head", "head128", "merge_select", "attention",
+                 "build_small"):
         tot, n = A.timing_read(name)
         kern[name] = dict(launches=n, avg_us=(tot * 1e3 / n) if n else None)
     wbytes = 2 if wl.wdtype == "bf16" else 4
-    one_launch = kern["head"]["launches"] == 0 and kern["build_small"]["launches"] > 0
+    one_launch = (kern["head"]["launches"] == 0 and kern["head128"]["launches"] == 0
+                  and kern["build_small"]["launches"] > 0)
+    # the dominant head kernel: the 128-row one when the batch has 128 rows (the
+    # first depths then run at their live width on the smaller kernels)
+    head_cls = "head128" if kern["head128"]["launches"] > 0 else "head"
     if one_launch:
         # a small fp32 head built in one launch: every depth reads U, W1 and W2
         head_us = kern["build_small"]["avg_us"]
         head_bytes = D * wbytes * (wl.d * wl.V + 8 * wl.d * wl.d)
     else:
-        head_us = kern["head"]["avg_us"]
+        head_us = kern[head_cls]["avg_us"]
         head_bytes = wbytes * wl.d * wl.V      # the output head, streamed once per launch
     achieved = head_bytes / (head_us * 1e-6) / 1e9
     log(f"[bench] head kernel {head_us:.1f} us/launch -> {achieved:.0f} GB/s; "
@@ -255,13 +260,13 @@ def main():
     rows_p = next(m for m in (16, 32, 64, 128) if m >= R * W)   # padded batch rows
     if one_launch:
         head_kernel = "k_build_small: all depths of the build in one launch"
+    elif head_cls == "head128":
+        head_kernel = ("k_head_rows128 (one 8-wave workgroup per compute unit, operands by LDS DMA, "
+                       "32x32x16 MFMA): the launches of the depths that run 128 rows")
     elif wl.wdtype != "bf16" or rows_p < 64:
         head_kernel = "k_head_bf16" if wl.wdtype == "bf16" else "k_head_f32"
-    elif rows_p == 64:
-        head_kernel = "k_head_wide (64 columns per wave, 64 rows)"
     else:
-        head_kernel = ("k_head_rows128 (one 8-wave workgroup per compute unit, operands by LDS DMA, "
-                       "32x32x16 MFMA)")
+        head_kernel = f"k_head_wide (64 columns per wave, {rows_p} rows)"
 
     # weights streamed per step: U (d V) + W1 and W2 (8 d^2) per depth, shared by R requests
     bytes_per_step = D * wbytes * (wl.d * wl.V + 8 * wl.d * wl.d)

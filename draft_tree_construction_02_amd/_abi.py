@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libdartree.so")
 DT_F32, DT_BF16 = 0, 1
 DT_LAYOUT_ROWMAJOR, DT_LAYOUT_PACKED = 0, 1
 KERNEL_CLASSES = {"gemm1": 0, "gemm2": 1, "head": 2, "merge_select": 3, "reduce": 4,
-                  "attention": 5, "build_small": 6}
+                  "attention": 5, "build_small": 6, "head128": 7}
 
 # every symbol include/dartree.h declares
 EXPORTS = [

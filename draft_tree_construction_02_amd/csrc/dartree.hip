@@ -121,8 +121,9 @@ struct StepWs {
   int runs1 = 0, runs2 = 0;    // balanced split-K grids (0: tiles of 128 columns)
 };
 
-StepWs carve_step(Carver& c, const dt_head* h, int rows, int k) {
-  StepWs w{};
+// Launch shape of the state update and head for `rows` rows: padded rows,
+// column tiles, split-K counts and balanced grids, vocabulary slices.
+void shape_step(StepWs& w, const dt_head* h, int rows) {
   const int bf = h->wdtype == DT_BF16;
   const int d = h->d, V = h->V;
   const int TN = gemm_tile_n(bf), KC = gemm_k_chunk(bf);
@@ -133,14 +134,31 @@ StepWs carve_step(Carver& c, const dt_head* h, int rows, int k) {
   w.tilesV = std::max(w.tilesV, head_tiles_for(h, w.Mp));   // slices of the launch, if more
   w.splits1 = choose_splits(d / KC, w.tiles1, w.Mp, d);
   w.splits2 = choose_splits(4 * d / KC, w.tiles2, w.Mp, 4 * d);
+  w.runs1 = w.runs2 = 0;
   if (bf) {
     choose_runs(d / KC, 4 * d, w.Mp, d, w.tiles1 * w.splits1, w.splits1, w.runs1);
     choose_runs(4 * d / KC, d, w.Mp, 4 * d, w.tiles2 * w.splits2, w.splits2, w.runs2);
   }
-  const size_t part1 = (size_t)w.splits1 * w.Mp * 4 * d;
-  const size_t part2 = (size_t)w.splits2 * w.Mp * d;
+}
+
+// Workspace of the state update + head for up to `rows` rows: buffers that
+// scale with the rows are sized for the largest padded count, the split-K
+// partials and per-slice head results for the largest over every padded
+// count up to it (a depth may run with fewer rows, so another launch shape).
+StepWs carve_step(Carver& c, const dt_head* h, int rows, int k) {
+  StepWs w{};
+  const int bf = h->wdtype == DT_BF16;
+  const int d = h->d;
+  size_t part = 0, slices = 0;
+  for (int m = 16;; m *= 2) {
+    shape_step(w, h, m < rows ? m : rows);
+    part = std::max(part, std::max((size_t)w.splits1 * w.Mp * 4 * d, (size_t)w.splits2 * w.Mp * d));
+    slices = std::max(slices, (size_t)w.Mp * w.tilesV);
+    if (m >= rows) break;
+  }
+  shape_step(w, h, rows);
   const size_t md = (size_t)w.Mp * d;
-  w.part = c.take<float>(part1 > part2 ? part1 : part2);
+  w.part = c.take<float>(part);
   if (bf) {
     w.H_hi = c.take<uint16_t>(4 * md);
     w.H_lo = c.take<uint16_t>(4 * md);
@@ -151,8 +169,8 @@ StepWs carve_step(Carver& c, const dt_head* h, int rows, int k) {
   } else {
     w.H = c.take<float>(4 * md);
   }
-  w.ms_part = c.take<float2>((size_t)w.Mp * w.tilesV);
-  w.key_part = c.take<uint64_t>((size_t)w.Mp * w.tilesV * k);
+  w.ms_part = c.take<float2>(slices);
+  w.key_part = c.take<uint64_t>(slices * k);
   w.ms2 = c.take<float2>((size_t)w.Mp * MERGE_SPLITS_MAX);
   w.key2 = c.take<uint64_t>((size_t)w.Mp * MERGE_SPLITS_MAX * kmax_for(k, false));
   w.cand_tok = c.take<int32_t>((size_t)w.Mp * k);
@@ -372,7 +390,8 @@ hipError_t run_head(const dt_head* hd, const StepWs& w, const float* s, int rows
   p.greedy = greedy;
   p.ms_part = w.ms_part;
   p.key_part = w.key_part;
-  hipError_t e = timed(DT_K_HEAD, st, [&] { return launch_head(p, st); });
+  const int cls = head_rows128_ok(p) ? DT_K_HEAD128 : DT_K_HEAD;
+  hipError_t e = timed(cls, st, [&] { return launch_head(p, st); });
   if (e != hipSuccess) return e;
   if (!final_merge)
     return timed(DT_K_MERGE, st, [&] {
@@ -531,26 +550,42 @@ int build_supertree_ex(const dt_head* head, const float* h, const float* s0,
                      bw.pre.cand_lp, bw.pre.lse, st);
     }
   }
+  // Frontier rows per request: the frontier of depth t holds at most
+  // min(W, keff^t) branches (the root alone at t = 0), so the plain build runs
+  // depth t with that many rows per request, padded to the launch's rows;
+  // the variants keep W rows throughout.
+  const int keff = greedy ? 1 : k;
+  const bool narrow = !markov && !base;
+  auto width = [&](int t) {
+    if (!narrow) return W;
+    long r = 1;
+    for (int i = 0; i < t && r < W; ++i) r *= keff;
+    return (int)std::min<long>(r, W);
+  };
   if (markov && e == hipSuccess) e = launch_markov_src(rows, W, w.Mp, bw.msrc, st);
   if (e == hipSuccess)
-    e = launch_beam_init(R, W, w.Mp, root_tok, w.tok[0], w.score[0], w.src[0], st);
+    e = launch_beam_init(R, width(0), padded_rows(R * width(0)), root_tok, w.tok[0], w.score[0],
+                         w.src[0], st);
   for (int t = 0; t < D && e == hipSuccess; ++t) {
     const int cur = t & 1, nxt = cur ^ 1;
+    const int rpr = width(t), rows_t = R * rpr;
+    StepWs wt = w;                      // same buffers, this depth's launch shape
+    shape_step(wt, head, rows_t);
     DepthIo io;
     io.s_prev = (t == 0 || markov) ? s0 : w.S[nxt];
     io.tok = w.tok[cur];
     io.src = markov ? bw.msrc : w.src[cur];
     io.h = h + (long)t * d;
     io.h_req_stride = (long)D * d;
-    io.rpr = W;
-    io.rows = rows;
+    io.rpr = rpr;
+    io.rows = rows_t;
     io.s_out = w.S[cur];
-    io.rows_out = rows;
-    e = run_update(head, w, io, st);
+    io.rows_out = rows_t;
+    e = run_update(head, wt, io, st);
     if (e != hipSuccess) break;
     // base candidates: the full merge gives each row's log-sum-exp, then the
     // children are chosen among the depth's candidates
-    e = run_head(head, w, w.S[cur], rows, k, T, w.cand_tok, w.cand_lp, w.lse, st, base);
+    e = run_head(head, wt, w.S[cur], rows_t, k, T, w.cand_tok, w.cand_lp, w.lse, st, base);
     if (e != hipSuccess) break;
     if (base) {
       CandArgs ca;
@@ -565,7 +600,7 @@ int build_supertree_ex(const dt_head* head, const float* h, const float* s0,
       ca.inv_T = greedy ? 1.f : (float)(1.0 / (double)T);
       ca.cand_tok = w.cand_tok;
       ca.cand_lp = w.cand_lp;
-      e = timed(DT_K_MERGE, st, [&] { return launch_cand_score(ca, rows, st); });
+      e = timed(DT_K_MERGE, st, [&] { return launch_cand_score(ca, rows_t, st); });
       if (e != hipSuccess) break;
     }
     BeamArgs b;
@@ -577,7 +612,7 @@ int build_supertree_ex(const dt_head* head, const float* h, const float* s0,
       b.ms2 = w.ms2;
       b.key2 = w.key2;
     }
-    b.S = merge_splits(head_tiles_for(head, w.Mp));
+    b.S = merge_splits(head_tiles_for(head, wt.Mp));
     b.kmax = kmax_for(k, greedy);
     b.score_in = w.score[cur];
     b.n_valid = n_valid;
@@ -587,7 +622,9 @@ int build_supertree_ex(const dt_head* head, const float* h, const float* s0,
     b.tok_out = w.tok[nxt];
     b.score_out = w.score[nxt];
     b.src_out = w.src[nxt];
-    b.Mp = w.Mp;
+    b.rpr_in = rpr;
+    b.rpr_out = width(t + 1);
+    b.Mp = padded_rows(R * b.rpr_out);
     e = timed(DT_K_MERGE, st, [&] { return launch_beam_step(b, st); });
   }
   return e == hipSuccess ? DT_OK : DT_EHIP;

@@ -170,7 +170,10 @@ struct BeamArgs {
   int32_t* tok_out = nullptr;          // [Mp]
   float* score_out = nullptr;          // [Mp]
   int32_t* src_out = nullptr;          // [Mp]
-  int Mp = 0;
+  int Mp = 0;                          // rows of the next depth's launches (padded)
+  // frontier rows per request of this depth (input rows r * rpr_in + i) and
+  // of the next one (output rows r * rpr_out + j); 0 means W
+  int rpr_in = 0, rpr_out = 0;
 };
 hipError_t launch_beam_init(int R, int W, int Mp, const int32_t* root_tok, int32_t* tok,
                             float* score, int32_t* src, hipStream_t st);

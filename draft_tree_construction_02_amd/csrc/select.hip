@@ -258,7 +258,8 @@ template <int KMAX>
 __global__ __launch_bounds__(BEAM_THREADS) void k_beam_step(BeamArgs b) {
   extern __shared__ uint64_t keys[];                       // [ncand]
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int base = r * b.W;
+  const int rin = b.rpr_in > 0 ? b.rpr_in : b.W, rout = b.rpr_out > 0 ? b.rpr_out : b.W;
+  const int base = r * rin, obase = r * rout;
   const int n_prev = b.t == 0 ? 1 : b.n_valid[r * b.D + b.t - 1];
   const int keff = b.greedy ? 1 : b.k;
   const int ncand = n_prev * keff;
@@ -282,9 +283,9 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_step(BeamArgs b) {
   // is read (rows past n_prev are ignored below), so these loads need not
   // wait for n_valid.
   constexpr int RPW = WAVE / 16;
-  for (int i0 = wave * RPW; b.ms2 && i0 < b.W; i0 += (BEAM_THREADS / WAVE) * RPW) {
+  for (int i0 = wave * RPW; b.ms2 && i0 < rin; i0 += (BEAM_THREADS / WAVE) * RPW) {
     const int sl = lane & 15, i = i0 + (lane >> 4);
-    const bool row_ok = i < b.W;
+    const bool row_ok = i < rin;
     const long o = (long)(base + (row_ok ? i : 0)) * b.S + sl;
     MaxSum tot{-INFINITY, 0.f};
     TopK<KMAX> all;
@@ -339,23 +340,25 @@ __global__ __launch_bounds__(BEAM_THREADS) void k_beam_step(BeamArgs b) {
       b.pool_tok[pool + rank] = tk;
       b.pool_parent[pool + rank] = b.t == 0 ? -1 : i;
       b.pool_score[pool + rank] = sc;
-      b.tok_out[base + rank] = tk;
-      b.score_out[base + rank] = sc;
-      b.src_out[base + rank] = base + i;
+      b.tok_out[obase + rank] = tk;
+      b.score_out[obase + rank] = sc;
+      b.src_out[obase + rank] = base + i;
     }
   }
   for (int j = nkeep + tid; j < b.W; j += BEAM_THREADS) {
     b.pool_tok[pool + j] = -1;
     b.pool_parent[pool + j] = -1;
     b.pool_score[pool + j] = -INFINITY;
-    b.tok_out[base + j] = -1;
-    b.score_out[base + j] = -INFINITY;
-    b.src_out[base + j] = -1;
+  }
+  for (int j = nkeep + tid; j < rout; j += BEAM_THREADS) {
+    b.tok_out[obase + j] = -1;
+    b.score_out[obase + j] = -INFINITY;
+    b.src_out[obase + j] = -1;
   }
   if (tid == 0) b.n_valid[r * b.D + b.t] = nkeep;
-  // padded rows beyond R*W stay empty
+  // padded rows beyond R * rpr_out stay empty
   if (r == 0)
-    for (int j = b.R * b.W + tid; j < b.Mp; j += BEAM_THREADS) {
+    for (int j = b.R * rout + tid; j < b.Mp; j += BEAM_THREADS) {
       b.tok_out[j] = -1;
       b.score_out[j] = -INFINITY;
       b.src_out[j] = -1;

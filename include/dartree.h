@@ -449,12 +449,14 @@ int hbm_read_probe(const void* buf, size_t bytes, uint64_t* sum, void* stream);
 typedef enum {
   DT_K_GEMM1 = 0,   /* state update, first projection (split-K partials)  */
   DT_K_GEMM2 = 1,   /* state update, second projection (split-K partials) */
-  DT_K_HEAD = 2,    /* corrected-logit head + per-tile softmax/top-k      */
+  DT_K_HEAD = 2,    /* corrected-logit head + per-tile softmax/top-k (the */
+                    /* 16- to 64-row and fp32 kernels)                    */
   DT_K_MERGE = 3,   /* per-row merge and per-request beam select          */
   DT_K_REDUCE = 4,  /* split-K reductions (GELU / residual epilogues)     */
   DT_K_ATTN = 5,    /* tree-attention verification layer (both kernels)   */
   DT_K_BUILD_SMALL = 6, /* one-launch build of a small fp32 head (all depths) */
-  DT_K_COUNT = 7
+  DT_K_HEAD128 = 7, /* corrected-logit head launches of the 128-row kernel */
+  DT_K_COUNT = 8
 } dt_kernel_class;
 
 /*
