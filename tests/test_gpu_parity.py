@@ -302,6 +302,59 @@ def test_prune_and_mask_match_oracle_on_random_pools(integer):
             assert np.array_equal(mask[r], O.tree_mask(vt.parent, vt.n, B))
 
 
+def _attention_case(n, P, Hq, Hkv, scale, seed, parents=None, key_gain=None):
+    """Run tree_attention_verify and the fp64 oracle on one seeded case."""
+    hd = 128
+    g = np.random.default_rng(seed)
+    if parents is None:
+        parents = np.array([-1] + [int(g.integers(-1, i)) for i in range(1, n)], np.int32)
+    mask = O.tree_mask(parents, n, n)
+    x = synth.make_verify_inputs(n, P, Hq, Hkv, hd, seed=seed)
+    if key_gain is not None:       # per-tree-key gain, applied before the bf16 rounding
+        kt = synth.bf16_bits_to_f32(x["k_tree"]) * np.asarray(key_gain, np.float32)[:, None, None]
+        x["k_tree"] = synth.bf16_bits(kt.astype(np.float32))
+    args = [bf16_dev(x[k]) for k in ("q", "k_prefix", "v_prefix", "k_tree", "v_tree")]
+    got = A.tree_attention_verify(*args, torch.from_numpy(mask.view(np.int32)).to(DEV), scale)
+    got = got.cpu().numpy()
+    f = lambda b: synth.bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
+    want = O.tree_attention(f(x["q"]), f(x["k_prefix"]), f(x["v_prefix"]), f(x["k_tree"]),
+                            f(x["v_tree"]), mask, n, scale)
+    return got, want
+
+
+@pytest.mark.parametrize("scale", [-1.0 / math.sqrt(128), 0.0])
+def test_tree_attention_negative_and_zero_scale(scale):
+    # a negative scale flips the order of the scores; scale 0 gives the
+    # uniform average over each query's visible keys
+    got, want = _attention_case(45, 200, 8, 2, scale, seed=11)
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - want))
+    assert err <= 1e-2 * np.max(np.abs(want)), err
+
+
+def test_tree_attention_large_scores_redo_pass():
+    # scale 1 on N(0,1) inputs: scores of std ~11 (16 in log2 units), so later
+    # key blocks exceed the first block's maximum by more than the rescale
+    # margin and passes are redone with a larger reference
+    got, want = _attention_case(40, 700, 8, 2, 1.0, seed=12)
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - want))
+    assert err <= 1e-2 * np.max(np.abs(want)), err
+
+
+def test_tree_attention_masked_large_keys_redo_pass():
+    # every node sees only itself (no prefix); odd nodes' keys are 60x larger,
+    # so the first block's raw maximum lies far above the visible score of an
+    # even node and its pass is redone with the visible maximum
+    n = 64
+    gain = np.where(np.arange(n) % 2 == 1, 60.0, 1.0)
+    got, want = _attention_case(n, 0, 4, 1, 1.0 / math.sqrt(128), seed=13,
+                                parents=np.full(n, -1, np.int32), key_gain=gain)
+    assert np.all(np.isfinite(got))
+    err = np.max(np.abs(got - want))
+    assert err <= 1e-2 * np.max(np.abs(want)), err
+
+
 @pytest.mark.parametrize("n,P,Hq,Hkv", [(37, 100, 8, 2), (128, 0, 4, 4), (70, 333, 32, 8)])
 def test_tree_attention_matches_oracle(n, P, Hq, Hkv):
     hd = 128
