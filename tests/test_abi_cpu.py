@@ -277,6 +277,12 @@ def test_stage_and_attention_validation():
     assert L.tree_attention_verify(*args, 128, 4096, 32, 8, 128, 0.1, 1, 1, 8, None) == DT_EWORKSPACE
     assert L.tree_attention_verify(None, 1, 1, 1, 1, 1, 128, 4096, 32, 8, 128, 0.1, 1, 1,
                                    1 << 40, None) == DT_EINVAL
+    # key offsets of the copies are 32-bit: 2^20 prefix keys x 8 heads x 256 B is refused
+    assert L.tree_attention_verify(*args, 128, 1 << 20, 32, 8, 128, 0.1, 1, 1, 1 << 40,
+                                   None) == DT_EUNSUPPORTED
+    # rows that fill the chip alone need no split of the key range, so no partials
+    assert L.tree_attention_workspace_size(1024, 0, 32, 8, 128) == 256
+    assert L.tree_attention_workspace_size(128, 4096, 32, 8, 128) > 256
 
 
 def test_timing_api_without_launches():

@@ -342,6 +342,16 @@ def test_tree_attention_large_scores_redo_pass():
     assert err <= 1e-2 * np.max(np.abs(want)), err
 
 
+def test_tree_attention_unsplit_key_range():
+    # 1024 nodes x 32 heads fill every compute unit with row blocks alone, so
+    # each workgroup takes the whole key range and writes the output directly
+    assert A.tree_attention_workspace_size(1024, 0, 32, 8, 128) == 256
+    got, want = _attention_case(1024, 0, 32, 8, 1.0 / math.sqrt(128), seed=14)
+    err = np.max(np.abs(got - want))
+    assert err <= 1e-2 * np.max(np.abs(want)), err
+    assert np.linalg.norm(got - want) <= 1e-2 * np.linalg.norm(want)
+
+
 def test_tree_attention_masked_large_keys_redo_pass():
     # every node sees only itself (no prefix); odd nodes' keys are 60x larger,
     # so the first block's raw maximum lies far above the visible score of an
