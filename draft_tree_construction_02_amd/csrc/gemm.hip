@@ -531,7 +531,14 @@ __global__ __launch_bounds__(128) void k_reduce(ReduceArgs r) {
   const long grp = gid / G;
   const int q = (int)(gid % G);
   const bool live = grp < (long)r.Mp * n8;   // no early exit: the butterfly needs every lane
-  const int m = live ? (int)(grp / n8) : 0, n = live ? (int)(grp % n8) * 8 : 0;
+  // 64 consecutive groups make one packed block (16 rows x 32 columns): group
+  // L of block b takes row 16 (b / (N / 32)) + L % 16, columns
+  // 32 (b % (N / 32)) + 8 (L / 16) .. + 7, so a wave's packed stores are
+  // contiguous and each row segment it reads is 128 bytes
+  const long blk = grp >> 6;
+  const int L = (int)(grp & 63), nb32 = r.N >> 5;
+  const int m = live ? 16 * (int)(blk / nb32) + (L & 15) : 0;
+  const int n = live ? 32 * (int)(blk % nb32) + 8 * (L >> 4) : 0;
   float y[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = 0.f;
@@ -571,6 +578,8 @@ __global__ __launch_bounds__(128) void k_reduce(ReduceArgs r) {
 }
 
 hipError_t launch_reduce(const ReduceArgs& r, hipStream_t st) {
+  // whole packed blocks: rows in 16s, columns in 32s
+  if (r.Mp % 16 != 0 || r.N % 32 != 0) return hipErrorInvalidValue;
   const long groups = (long)r.Mp * (r.N / 8);
   const int G = r.splits >= 12 ? 4 : (r.splits >= 3 ? 2 : 1);
   const unsigned blocks = (unsigned)((groups * G + 127) / 128);
