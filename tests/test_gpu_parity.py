@@ -49,6 +49,12 @@ def small_cases():
         "bf16_rows40_T0": synth.Workload("bf16_rows40_T0", V=2048, d=256, wdtype="bf16", D=3,
                                          W=8, k=4, B=3, beta=0.0, T=0.0, R=5,
                                          seeds=(17, 18, 19, 20, 21)),
+        # 128 rows from depth 3 on (8 requests x 16; depths 1 and 2 at 8 and 64
+        # live rows): the 128-row head (packed) or the 64-column head
+        # (row-major), the 128-row state update, a ragged vocabulary tile
+        "bf16_rows128": synth.Workload("bf16_rows128", V=3001, d=256, wdtype="bf16", D=4, W=16,
+                                       k=8, B=40, beta=-0.05, T=1.0, R=8,
+                                       seeds=tuple(range(40, 48))),
     }
 
 
