@@ -253,7 +253,7 @@ constexpr int S8_NCW = S8_NC / 2;                  // tiles per wave (half a sli
 constexpr int S8_FPW = 2 * S8_NC / S8_WAVES;       // weight fragments per wave per step
 constexpr int S8_WSLOT = 2 * S8_NC * R8_BLK;       // bf16 per weight slot
 constexpr int S8_ASLOT = 16 * R8_BLK;              // bf16 per activation slot
-constexpr int S8_CAND = 20;
+constexpr int S8_CAND = 19;                        // candidates per lane before the full insertion
 
 // Workgroups of the head: one per compute unit (fewer for a small
 // vocabulary, at least 128 columns each), each slice at most S8_NC tiles.
@@ -480,10 +480,16 @@ void k_head_rows128(HeadArgs p) {
       }
     }
     const float tau = top[KMAX - 1];
-    static_assert(S8_CAND == 20 && 10 * 64 * S8_WAVES * 8 <= S8_WSLOT * 2, "candidate space");
-    uint64_t* cand0 = (uint64_t*)W0;
-    uint64_t* cand1 = (uint64_t*)W1;
-    const int tid = threadIdx.x;
+    // Candidate slots of the lane in W0 (waves 0..3) or W1 (waves 4..7):
+    // values in the first half, columns in the second, slot j of thread t at
+    // word 256 j + t % 256 of each half; slot S8_CAND takes the values that
+    // are not kept.  Every value is written to the slot the count points at
+    // and the count advances only for a value >= tau, so the scan has no
+    // branch (a branch per value compiled to an exec-mask save and two taken
+    // jumps each).
+    static_assert(2 * (S8_CAND + 1) * 256 * 4 <= S8_WSLOT * 2, "candidate space");
+    float* cval = (float*)(hf ? W1 : W0) + (threadIdx.x & 255);
+    uint32_t* ccol = (uint32_t*)(hf ? W1 : W0) + (S8_CAND + 1) * 256 + (threadIdx.x & 255);
     int cnt = 0;
     if (tau > -INFINITY) {
 #pragma unroll
@@ -491,12 +497,10 @@ void k_head_rows128(HeadArgs p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float v = acc[c][e];
-          if (v >= tau) {
-            if (cnt < S8_CAND)
-              (cnt < 10 ? cand0 : cand1)[(cnt < 10 ? cnt : cnt - 10) * 64 * S8_WAVES + tid] =
-                  make_key(v, (uint32_t)(col0 + 32 * c + 8 * (e >> 2) + (e & 3)));
-            ++cnt;
-          }
+          const int o = 256 * min(cnt, S8_CAND);
+          cval[o] = v;
+          ccol[o] = (uint32_t)(col0 + 32 * c + 8 * (e >> 2) + (e & 3));
+          cnt += v >= tau ? 1 : 0;
         }
     } else {
       cnt = S8_CAND + 1;
@@ -509,7 +513,7 @@ void k_head_rows128(HeadArgs p) {
       n = __builtin_amdgcn_readfirstlane(n);
       for (int i = 0; i < n; ++i) {
         uint64_t key = 0;
-        if (i < cnt) key = (i < 10 ? cand0 : cand1)[(i < 10 ? i : i - 10) * 64 * S8_WAVES + tid];
+        if (i < cnt) key = make_key(cval[256 * i], ccol[256 * i]);
         tk.insert(key);
       }
     }
@@ -528,11 +532,14 @@ void k_head_rows128(HeadArgs p) {
   }
   float sum = 0.f;
   if (!p.greedy) {
+    // e^(v - m0) as the hardware 2^x of (v - m0) log2(e): (v - m0) is within
+    // the fp32 rounding of the value, the product adds one rounding
     const float m0 = mx > -INFINITY ? mx : 0.f;
 #pragma unroll
     for (int c = 0; c < S8_NCW; ++c)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sum += expf(acc[c][e] - m0);
+      for (int e = 0; e < 16; ++e)
+        sum += __builtin_amdgcn_exp2f((acc[c][e] - m0) * 1.44269504088896341f);
   }
   MaxSum ms{mx, sum};
   {
