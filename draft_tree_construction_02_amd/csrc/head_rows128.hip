@@ -488,19 +488,23 @@ void k_head_rows128(HeadArgs p) {
     // branch (a branch per value compiled to an exec-mask save and two taken
     // jumps each).
     static_assert(2 * (S8_CAND + 1) * 256 * 4 <= S8_WSLOT * 2, "candidate space");
+    constexpr int SLOTB = 256 * 4, COLB = (S8_CAND + 1) * SLOTB;     // bytes
     float* cval = (float*)(hf ? W1 : W0) + (threadIdx.x & 255);
     uint32_t* ccol = (uint32_t*)(hf ? W1 : W0) + (S8_CAND + 1) * 256 + (threadIdx.x & 255);
     int cnt = 0;
     if (tau > -INFINITY) {
+      char* const cb = (char*)cval;
+      int off = 0;                                   // SLOTB * min(kept, S8_CAND)
 #pragma unroll
       for (int c = 0; c < S8_NCW; ++c)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const float v = acc[c][e];
-          const int o = 256 * min(cnt, S8_CAND);
-          cval[o] = v;
-          ccol[o] = (uint32_t)(col0 + 32 * c + 8 * (e >> 2) + (e & 3));
-          cnt += v >= tau ? 1 : 0;
+          *(float*)(cb + off) = v;
+          *(uint32_t*)(cb + off + COLB) = (uint32_t)(col0 + 32 * c + 8 * (e >> 2) + (e & 3));
+          const bool keep = v >= tau;
+          cnt += keep ? 1 : 0;
+          off = min(off + (keep ? SLOTB : 0), S8_CAND * SLOTB);
         }
     } else {
       cnt = S8_CAND + 1;
