@@ -592,26 +592,109 @@ hipError_t launch_reduce(const ReduceArgs& r, hipStream_t st) {
 // ----------------------------------------------------------------------------
 // corrected-logit head with fused per-tile log-softmax statistics and top-k
 // ----------------------------------------------------------------------------
-template <int MT, int KMAX, int TN, int THREADS>
+// Compare-exchange keeping the larger key in a.
+__device__ __forceinline__ void ce_desc(uint64_t& a, uint64_t& b) {
+  const bool sw = b > a;
+  const uint64_t hi = sw ? b : a, lo = sw ? a : b;
+  a = hi;
+  b = lo;
+}
+
+// Bitonic sorting network over N keys (N a power of two), descending.
+template <int N>
+__device__ __forceinline__ void bitonic_sort_desc(uint64_t (&a)[N]) {
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1)
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          if ((i & size) == 0) ce_desc(a[i], a[j]);
+          else ce_desc(a[j], a[i]);
+        }
+      }
+}
+
+// The K largest of NV keys (NV a power of two; key 0 marks an empty entry):
+// K = 1 is a maximum; otherwise runs of min(K, NV) keys are sorted by a
+// network and folded in with the bitonic merge.  Keys are distinct (the
+// column is part of them), so the list equals K one-at-a-time insertions.
+template <int K, int NV>
+__device__ __forceinline__ void topk_of(TopK<K>& tk, uint64_t (&keys)[NV]) {
+  if constexpr (K == 1) {
+    uint64_t m = keys[0];
+#pragma unroll
+    for (int j = 1; j < NV; ++j) m = keys[j] > m ? keys[j] : m;
+    tk.v[0] = m;
+  } else {
+    constexpr int R = NV < K ? NV : K;
+#pragma unroll
+    for (int c = 0; c < NV / R; ++c) {
+      uint64_t run[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) run[i] = keys[c * R + i];
+      bitonic_sort_desc<R>(run);
+      if (c == 0) {
+#pragma unroll
+        for (int i = 0; i < K; ++i) tk.v[i] = i < R ? run[i] : 0ull;
+      } else {
+        if constexpr (R == K) tk.merge(run);    // more than one run only when NV > K
+      }
+    }
+  }
+}
+
+// Per-row (max, sum exp) and top-k keys of the logit tile in LDS: G threads
+// per row, thread q holding columns q, q + G, ... of the tile.  FASTEXP takes
+// e^x as the hardware 2^x of x log2(e) (bf16 heads); otherwise expf.
+template <int MT, int KMAX, int TN, int THREADS, bool FASTEXP>
 __device__ __forceinline__ void head_epilogue(const HeadArgs& p, const float* Cs, int tile, int n0,
                                               int nvalid) {
   constexpr int Mp = 16 * MT;
   constexpr int G = THREADS / Mp;         // threads per row (power of two <= 64)
   static_assert(G >= 1 && G <= 64, "row group must fit in a wave");
+  constexpr int NV = TN / G;              // columns per thread
+  static_assert(NV >= 1 && (NV & (NV - 1)) == 0 && NV * G == TN, "columns per thread");
   const int tid = threadIdx.x, m = tid / G, q = tid % G;
   const int ntiles = gridDim.x;
   const float* row = Cs + m * (TN + CPAD);
-  float mx = -INFINITY;
+  auto ex = [](float x) {
+    return FASTEXP ? __builtin_amdgcn_exp2f(x * 1.44269504088896341f) : expf(x);
+  };
+  float mx = -INFINITY, s = 0.f;
   TopK<KMAX> tk;
-  tk.clear();
-  for (int n = q; n < nvalid; n += G) {
-    const float v = row[n];
-    mx = fmaxf(mx, v);
-    tk.insert(make_key(v, (uint32_t)(n0 + n)));
+  if constexpr (NV <= 16) {
+    // the thread's columns in registers, top-k by a sorting network
+    float v[NV];
+    uint64_t keys[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int n = q + G * j;
+      const bool ok = n < nvalid;
+      v[j] = ok ? row[n] : -INFINITY;
+      keys[j] = ok ? make_key(v[j], (uint32_t)(n0 + n)) : 0ull;
+      mx = fmaxf(mx, v[j]);
+    }
+    topk_of<KMAX, NV>(tk, keys);
+    if (!p.greedy) {
+      // empty entries are -inf and add +0
+      const float m0 = mx > -INFINITY ? mx : 0.f;
+#pragma unroll
+      for (int j = 0; j < NV; ++j) s += ex(v[j] - m0);
+    }
+  } else {
+    // many columns per thread (64 and 128 rows): one key at a time
+    tk.clear();
+    for (int n = q; n < nvalid; n += G) {
+      const float v = row[n];
+      mx = fmaxf(mx, v);
+      tk.insert(make_key(v, (uint32_t)(n0 + n)));
+    }
+    if (!p.greedy)
+      for (int n = q; n < nvalid; n += G) s += ex(row[n] - mx);
   }
-  float s = 0.f;
-  if (!p.greedy)
-    for (int n = q; n < nvalid; n += G) s += expf(row[n] - mx);
   MaxSum ms{mx, s};
   for (int off = 1; off < G; off <<= 1) {
     const float m2 = __shfl_xor(ms.m, off, WAVE);
@@ -667,7 +750,7 @@ __attribute__((amdgpu_waves_per_eu(DT_HEAD_WPE, 8))) void k_head_bf16(HeadArgs p
           make_float4(v[0] * scale, v[1] * scale, v[2] * scale, v[3] * scale);
     }
   __syncthreads();
-  head_epilogue<MT, KMAX, TN, 64 * DT_WV_HEAD>(p, Cs, tile, n0, min(TN, col_end - n0));
+  head_epilogue<MT, KMAX, TN, 64 * DT_WV_HEAD, true>(p, Cs, tile, n0, min(TN, col_end - n0));
 }
 
 template <int MT, int KMAX>
@@ -677,7 +760,7 @@ __global__ __launch_bounds__(NT) void k_head_f32(HeadArgs p) {
   const int tile = blockIdx.x;
   const float* Cs = tile_f32<MT, false>(p.a, (const float*)p.Ut, p.d, p.V, tile * TN_F, 0, p.d,
                                         p.greedy ? 1.f : p.inv_T, smem);
-  head_epilogue<MT, KMAX, TN_F, NT>(p, Cs, tile, tile * TN_F, min(TN_F, p.V - tile * TN_F));
+  head_epilogue<MT, KMAX, TN_F, NT, false>(p, Cs, tile, tile * TN_F, min(TN_F, p.V - tile * TN_F));
 }
 
 // ----------------------------------------------------------------------------
