@@ -106,10 +106,13 @@ struct TopK {
 // (max, sum exp(x - max)) pair, combined in a fixed order.
 struct MaxSum {
   float m, s;
+  // e^(m - M) as the hardware 2^x of (m - M) log2(e); the exponent is <= 0,
+  // and -inf (an empty part) gives 0
   __device__ __forceinline__ void combine(float m2, float s2) {
     float M = fmaxf(m, m2);
     if (M == -INFINITY) { m = M; s = 0.f; return; }
-    s = s * expf(m - M) + s2 * expf(m2 - M);
+    s = s * __builtin_amdgcn_exp2f((m - M) * 1.44269504088896341f) +
+        s2 * __builtin_amdgcn_exp2f((m2 - M) * 1.44269504088896341f);
     m = M;
   }
 };

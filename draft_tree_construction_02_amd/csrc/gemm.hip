@@ -696,10 +696,15 @@ __device__ __forceinline__ void head_epilogue(const HeadArgs& p, const float* Cs
       for (int n = q; n < nvalid; n += G) s += ex(row[n] - mx);
   }
   MaxSum ms{mx, s};
-  for (int off = 1; off < G; off <<= 1) {
-    const float m2 = __shfl_xor(ms.m, off, WAVE);
-    const float s2 = __shfl_xor(ms.s, off, WAVE);
-    ms.combine(m2, s2);
+  if (p.greedy) {
+    // T = 0 uses the maximum alone (the sums stay 0)
+    for (int off = 1; off < G; off <<= 1) ms.m = fmaxf(ms.m, __shfl_xor(ms.m, off, WAVE));
+  } else {
+    for (int off = 1; off < G; off <<= 1) {
+      const float m2 = __shfl_xor(ms.m, off, WAVE);
+      const float s2 = __shfl_xor(ms.s, off, WAVE);
+      ms.combine(m2, s2);
+    }
   }
   tk.reduce_lanes(G);
   if (q == 0) {
