@@ -201,7 +201,14 @@ def test_build_is_deterministic(name, packed, R, W, multi_kernel):
     ("bf16_k16", 128, 16, 1.3, True), ("bf16_ragged_rows", 128, 3, 0.7, True),
     ("bf16_T0", 128, 4, 0.0, True), ("bf16_T1", 100, 4, 1.0, True),
     ("bf16_T0", 7, 8, 0.0, True), ("bf16_ragged_rows", 50, 3, 0.7, False),
-    ("tiny", 4, 4, 1.0, False), ("f32_wide", 70, 5, 1.0, False)])
+    ("tiny", 4, 4, 1.0, False), ("f32_wide", 70, 5, 1.0, False),
+    # the <=32-row epilogue's top-k by sorting network: 8 columns per thread
+    # (16 rows) with k = 16 (one padded run), 16 columns (32 rows) with k = 4
+    # (four runs folded by merges), k = 16 (one run), k = 1 at T > 0 (maximum);
+    # the fp32 head at 16 and 32 rows (4 and 8 columns per thread)
+    ("bf16_T1", 16, 16, 1.0, True), ("bf16_T1", 32, 4, 1.0, False),
+    ("bf16_k16", 30, 16, 1.3, True), ("bf16_T1", 25, 1, 1.0, True),
+    ("tiny", 16, 8, 1.0, False), ("f32_wide", 30, 5, 1.0, False)])
 def test_corrected_topk_matches_oracle(name, rows, k, T, packed):
     wl = small_cases()[name]
     hw, _, head, ohead = case_inputs(wl, packed)
