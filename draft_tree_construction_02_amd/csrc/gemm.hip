@@ -592,60 +592,6 @@ hipError_t launch_reduce(const ReduceArgs& r, hipStream_t st) {
 // ----------------------------------------------------------------------------
 // corrected-logit head with fused per-tile log-softmax statistics and top-k
 // ----------------------------------------------------------------------------
-// Compare-exchange keeping the larger key in a.
-__device__ __forceinline__ void ce_desc(uint64_t& a, uint64_t& b) {
-  const bool sw = b > a;
-  const uint64_t hi = sw ? b : a, lo = sw ? a : b;
-  a = hi;
-  b = lo;
-}
-
-// Bitonic sorting network over N keys (N a power of two), descending.
-template <int N>
-__device__ __forceinline__ void bitonic_sort_desc(uint64_t (&a)[N]) {
-#pragma unroll
-  for (int size = 2; size <= N; size <<= 1)
-#pragma unroll
-    for (int stride = size / 2; stride > 0; stride >>= 1)
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int j = i ^ stride;
-        if (j > i) {
-          if ((i & size) == 0) ce_desc(a[i], a[j]);
-          else ce_desc(a[j], a[i]);
-        }
-      }
-}
-
-// The K largest of NV keys (NV a power of two; key 0 marks an empty entry):
-// K = 1 is a maximum; otherwise runs of min(K, NV) keys are sorted by a
-// network and folded in with the bitonic merge.  Keys are distinct (the
-// column is part of them), so the list equals K one-at-a-time insertions.
-template <int K, int NV>
-__device__ __forceinline__ void topk_of(TopK<K>& tk, uint64_t (&keys)[NV]) {
-  if constexpr (K == 1) {
-    uint64_t m = keys[0];
-#pragma unroll
-    for (int j = 1; j < NV; ++j) m = keys[j] > m ? keys[j] : m;
-    tk.v[0] = m;
-  } else {
-    constexpr int R = NV < K ? NV : K;
-#pragma unroll
-    for (int c = 0; c < NV / R; ++c) {
-      uint64_t run[R];
-#pragma unroll
-      for (int i = 0; i < R; ++i) run[i] = keys[c * R + i];
-      bitonic_sort_desc<R>(run);
-      if (c == 0) {
-#pragma unroll
-        for (int i = 0; i < K; ++i) tk.v[i] = i < R ? run[i] : 0ull;
-      } else {
-        if constexpr (R == K) tk.merge(run);    // more than one run only when NV > K
-      }
-    }
-  }
-}
-
 // Per-row (max, sum exp) and top-k keys of the logit tile in LDS: G threads
 // per row, thread q holding columns q, q + G, ... of the tile.  FASTEXP takes
 // e^x as the hardware 2^x of x log2(e) (bf16 heads); otherwise expf.

@@ -515,10 +515,23 @@ void k_head_rows128(HeadArgs p) {
 #pragma unroll
       for (int m = 1; m < WAVE; m <<= 1) n = max(n, __shfl_xor(n, m, WAVE));
       n = __builtin_amdgcn_readfirstlane(n);
-      for (int i = 0; i < n; ++i) {
-        uint64_t key = 0;
-        if (i < cnt) key = make_key(cval[256 * i], ccol[256 * i]);
-        tk.insert(key);
+      // the candidates in runs of KMAX (empty keys past the lane's count),
+      // each sorted by a network and folded in by a bitonic merge
+      for (int r0 = 0; r0 < n; r0 += KMAX) {
+        uint64_t run[KMAX];
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) {
+          const int j = r0 + i;
+          run[i] = j < cnt ? make_key(cval[256 * j], ccol[256 * j]) : 0ull;
+        }
+        TopK<KMAX> part;
+        topk_of<KMAX, KMAX>(part, run);
+        if (r0 == 0) {
+#pragma unroll
+          for (int i = 0; i < KMAX; ++i) tk.v[i] = part.v[i];
+        } else {
+          tk.merge(part.v);
+        }
       }
     }
   }
