@@ -310,16 +310,29 @@ def main():
         "step_weight_stream_gbs": round(bytes_per_step / (ms_per_step * 1e-3) / 1e9, 1),
     }
 
+    # the extra legs below report beside the headline; if one of them fails,
+    # the line still carries the measurement, with the failure in its field
+    def leg(name, fn):
+        try:
+            return fn()
+        except Exception as exc:          # noqa: BLE001 - recorded in the line, not hidden
+            log(f"[bench] {name} failed: {type(exc).__name__}: {exc}")
+            return {"error": f"{type(exc).__name__}: {exc}"[:300]}
+
     seq_tree = None
     if wl.R == 1 and not args.no_sequential:
-        res["sequential_baseline"], seq_tree = sequential_baseline(A, head, h, s0, root, wl, b_ms,
-                                                                   b_wall, bpm_ms, bpm_wall,
-                                                                   args.steps)
+        out = leg("sequential baseline", lambda: sequential_baseline(
+            A, head, h, s0, root, wl, b_ms, b_wall, bpm_ms, bpm_wall, args.steps))
+        if isinstance(out, tuple):
+            res["sequential_baseline"], seq_tree = out
+        else:
+            res["sequential_baseline"] = out
     if not args.no_walk:
-        res["acceptance"] = acceptance(A, synth, hw, wl, up, h, s0, root, pool, sel, seq_tree)
+        res["acceptance"] = leg("acceptance walk", lambda: acceptance(
+            A, synth, hw, wl, up, h, s0, root, pool, sel, seq_tree))
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, hw, req, max(args.cpu_builds, wl.R),
-                                           args.cpu_budget_s)
+        res["cpu_baseline"] = leg("cpu baseline", lambda: cpu_baseline(
+            wl, hw, req, max(args.cpu_builds, wl.R), args.cpu_budget_s))
     print(json.dumps(res), flush=True)
 
 
