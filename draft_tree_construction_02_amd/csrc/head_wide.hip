@@ -1,11 +1,16 @@
 // Corrected-logit head for many surviving branches (64 or 128 rows), gfx950.
 //
-// Same contract as the head in gemm.hip (y = s' U / T over one 256-column
-// slice of the vocabulary per workgroup, per-row (max, sum exp) and top-k
-// keys of the slice written as partials), shaped for the case where the
-// activation is large: every wave owns 64 columns (4 tiles of 16) for all
-// rows, so each activation fragment read from LDS feeds 4 weight tiles and
-// the LDS read traffic is a quarter of the weight-tile count x rows.  The
+// Same contract as the head in gemm.hip (y = s' U / T over one slice of the
+// vocabulary per workgroup, per-row (max, sum exp) and top-k keys of the
+// slice written as partials), shaped for the case where the activation is
+// large: every wave owns NW tiles of 16 columns for all rows, so each
+// activation fragment read from LDS feeds NW weight tiles.  The slices are
+// balanced runs of 16-column tiles: at 64 rows two workgroups per compute
+// unit with 5 tiles per wave (18-19 tiles per slice at V = 151936, all
+// workgroups resident at once), at 128 rows runs of at most 16 tiles with 4
+// per wave.  A run may cross the packed layout's row groups, so every tile
+// has its own block offset; a wave's tiles past its slice re-read the
+// slice's last tile (in bounds, never reported).  The
 // weight fragments of the next 64-K chunk are requested right after the
 // MFMAs of the current one consume theirs, and the activation chunk is
 // double-buffered in LDS with a single barrier per chunk, so two waves per
@@ -28,8 +33,9 @@ namespace {
 #endif
 
 constexpr int HW_WAVES = 4;                       // waves per workgroup
-constexpr int HW_NW = 4;                          // 16-column tiles per wave
-constexpr int HW_TN = HW_WAVES * HW_NW * 16;      // columns per workgroup
+// 16-column tiles per wave: 5 at 64 rows, 4 at 128 rows (register budget of
+// two waves per SIMD)
+constexpr int hw_nw(int MT) { return MT <= 4 ? 5 : 4; }
 constexpr int HW_BLK = 512;                       // bf16 per packed 1 KB block
 constexpr int HW_STEPS = 2;                       // 32-K steps per staged chunk
 
@@ -74,12 +80,16 @@ __device__ __forceinline__ void hw_store_a(const u32x4 (&v)[N], uint16_t* buf, i
     *(u32x4*)(buf + (wave + HW_WAVES * i) * HW_BLK + lane * 8) = v[i];
 }
 
-// Weight fragments of one K step for the wave's 4 tiles; `wp` points at the
-// step's block of the wave's first tile in the grouped packed layout (the
-// wave's 4 tiles are consecutive blocks there).
-__device__ __forceinline__ void hw_load_b(u32x4 (&b)[HW_NW], const uint16_t* wp) {
+// Weight fragments of one K step for the wave's NW tiles: tile c's block of
+// the step starts toff[c] + kofs bytes into the grouped packed layout (both
+// wave-uniform, so they stay in scalar registers), the lane's 16 bytes at
+// vlane.  Non-temporal: the head's weights are streamed once per depth.
+template <int NW>
+__device__ __forceinline__ void hw_load_b(u32x4 (&b)[NW], __amdgpu_buffer_rsrc_t wrs, int vlane,
+                                          const uint32_t (&toff)[NW], uint32_t kofs) {
 #pragma unroll
-  for (int c = 0; c < HW_NW; ++c) b[c] = __builtin_nontemporal_load((const u32x4*)(wp + c * HW_BLK));
+  for (int c = 0; c < NW; ++c)
+    b[c] = __builtin_amdgcn_raw_buffer_load_b128(wrs, vlane, toff[c] + kofs, 2 /* nt */);
 }
 
 template <int MT, int KMAX>
@@ -92,23 +102,37 @@ __attribute__((amdgpu_waves_per_eu(2))) void k_head_wide(HeadArgs p) {
   uint16_t* As = (uint16_t*)smem;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tile = blockIdx.x, n0 = tile * HW_TN;
+  constexpr int NW = hw_nw(MT);
+  const int tile = blockIdx.x;
 
-  // this wave's first 16-column tile and its place in the grouped layout.
-  // Tiles past V inside the last row group are stored zero rows; a wave whose
-  // tiles all lie past the stored groups streams the last stored tiles
-  // instead (their columns are >= V and never reach the epilogue), so every
-  // weight load is unconditional and in bounds.
+  // this slice: 16-column tiles [tb, te) of the nt16 = ceil(V / 16), the
+  // host's grid leaving 1 .. HW_WAVES NW tiles per slice.  Wave w owns tiles
+  // tw .. tw + NW - 1; those at or past te load tile te - 1 again (its
+  // columns are masked in the epilogue), so every weight load is
+  // unconditional and in bounds (tiles below te lie in the stored groups).
+  const int nt16 = (p.V + 15) / 16;
+  const int tb = (int)((long)tile * nt16 / gridDim.x);
+  const int te = (int)((long)(tile + 1) * nt16 / gridDim.x);
+  const int tw = tb + wave * NW;
+  // byte offsets fit 32 unsigned bits: the host admits heads of < 4 GiB
   const int tpg = PACK_ROWS / 16, kblocks = p.d / 32;
-  const int stored_tiles = (p.V + PACK_ROWS - 1) / PACK_ROWS * tpg;
-  const int t0 = min(n0 / 16 + wave * HW_NW, stored_tiles - HW_NW);
-  const uint16_t* wp = (const uint16_t*)p.Ut +
-                       (((long)(t0 / tpg) * kblocks) * tpg + t0 % tpg) * HW_BLK + lane * 8;
-  constexpr int WSTEP = (PACK_ROWS / 16) * HW_BLK;     // one K step of a row group
-
-  f32x4 acc[HW_NW][MT];
+  const uint32_t wbytes = (uint32_t)((size_t)(nt16 + tpg - 1) / tpg * tpg * 16 * p.d * 2);
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.Ut, (short)0, (int)wbytes, 0x00020000);
+  uint32_t toff[NW];
 #pragma unroll
-  for (int c = 0; c < HW_NW; ++c)
+  for (int c = 0; c < NW; ++c) {
+    const int t = min(tw + c, te - 1);
+    toff[c] = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(((t / tpg) * kblocks * tpg + t % tpg) * (uint32_t)(HW_BLK * 2)));
+  }
+  const int vlane = lane * 16;
+  uint32_t kofs = 0;
+  constexpr uint32_t WSTEP = (PACK_ROWS / 16) * HW_BLK * 2;     // bytes of one K step of a row group
+
+  f32x4 acc[NW][MT];
+#pragma unroll
+  for (int c = 0; c < NW; ++c)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[c][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -117,12 +141,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void k_head_wide(HeadArgs p) {
   hw_a_ptrs<MT>(ap, p.pa, wave, lane);
   // weight fragments of RING chunks in flight: slot (ch % RING, j)
   constexpr int RING = DT_HW_RING;
-  u32x4 b[RING][HW_STEPS][HW_NW];
+  u32x4 b[RING][HW_STEPS][NW];
   u32x4 av[C::ABLK];
 #pragma unroll
   for (int r = 0; r < RING; ++r)
 #pragma unroll
-    for (int j = 0; j < HW_STEPS; ++j, wp += WSTEP) hw_load_b(b[r][j], wp);
+    for (int j = 0; j < HW_STEPS; ++j, kofs += WSTEP) hw_load_b(b[r][j], wrs, vlane, toff, kofs);
   hw_load_a(av, ap, 0);
   hw_store_a(av, As, wave, lane);
   __syncthreads();
@@ -164,17 +188,17 @@ __attribute__((amdgpu_waves_per_eu(2))) void k_head_wide(HeadArgs p) {
             bf16x8, *(const u32x4*)(cur + ((MT + mt) * 2 + j) * HW_BLK + lane * 8));
 #endif
 #pragma unroll
-        for (int c = 0; c < HW_NW; ++c)
+        for (int c = 0; c < NW; ++c)
           acc[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8, b[R][j][c]), ahi, acc[c][mt], 0, 0, 0);
 #pragma unroll
-        for (int c = 0; c < HW_NW; ++c)
+        for (int c = 0; c < NW; ++c)
           acc[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8, b[R][j][c]), alo, acc[c][mt], 0, 0, 0);
       }
       if (LOADB) {
-        hw_load_b(b[R][j], wp);
-        wp += WSTEP;
+        hw_load_b(b[R][j], wrs, vlane, toff, kofs);
+        kofs += WSTEP;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -199,26 +223,27 @@ __attribute__((amdgpu_waves_per_eu(2))) void k_head_wide(HeadArgs p) {
     chunk(ch + 1, S1{}, F{}, F{});
   }
 
-  // per-row statistics of the wave's 64 columns: lane l holds row 16 mt + l % 16,
-  // columns 16 c + 4 (l / 16) + i; the 4 lanes of a row combine by butterfly
+  // per-row statistics of the wave's tiles: lane l holds row 16 mt + l % 16,
+  // columns 16 (tw + c) + 4 (l / 16) + i, those below min(16 te, V) valid;
+  // the 4 lanes of a row combine by butterfly
   float2* ms_l = (float2*)smem;                                   // [wave][Mp]
   uint64_t* key_l = (uint64_t*)(smem + HW_WAVES * Mp * 8);        // [wave][Mp][KMAX]
   const float scale = p.greedy ? 1.f : p.inv_T;
   const int r = lane & 15, q = lane >> 4;
-  const int colw = n0 + wave * HW_NW * 16 + 4 * q;
+  const int colw = 16 * tw + 4 * q, colend = min(16 * te, p.V);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    float v[HW_NW][4];
+    float v[NW][4];
     float mx = -INFINITY;
     TopK<KMAX> tk;
     tk.clear();
 #pragma unroll
-    for (int c = 0; c < HW_NW; ++c)
+    for (int c = 0; c < NW; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int col = colw + 16 * c + i;
         v[c][i] = acc[c][mt][i] * scale;
-        if (col < p.V) {
+        if (col < colend) {
           mx = fmaxf(mx, v[c][i]);
           tk.insert(make_key(v[c][i], (uint32_t)col));
         }
@@ -226,10 +251,10 @@ __attribute__((amdgpu_waves_per_eu(2))) void k_head_wide(HeadArgs p) {
     float s = 0.f;
     if (!p.greedy) {
 #pragma unroll
-      for (int c = 0; c < HW_NW; ++c)
+      for (int c = 0; c < NW; ++c)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (colw + 16 * c + i < p.V) s += expf(v[c][i] - mx);
+          if (colw + 16 * c + i < colend) s += expf(v[c][i] - mx);
     }
     MaxSum ms{mx, s};
 #pragma unroll
@@ -289,9 +314,21 @@ __attribute__((amdgpu_waves_per_eu(2))) void k_head_wide(HeadArgs p) {
   }
 }
 
+// Slices of the head: at 64 rows two workgroups per compute unit (more when
+// V needs runs longer than 4 NW tiles, fewer for a small vocabulary, at
+// least ~10 tiles each); at 128 rows runs of at most 16 tiles.  Every slice
+// holds 1 .. 4 NW tiles.
+int hw_slices(int Mp, int V) {
+  const int nt16 = (V + 15) / 16;
+  const int per = HW_WAVES * hw_nw(Mp / 16);
+  const int need = (nt16 + per - 1) / per;
+  if (Mp > 64) return need;
+  return std::max(need, std::min(2 * device_cu_count(), std::max(1, nt16 / 10)));
+}
+
 template <int MT, int KMAX>
 hipError_t head_wide_mk(const HeadArgs& p, hipStream_t st) {
-  const dim3 grid((p.V + HW_TN - 1) / HW_TN);
+  const dim3 grid(hw_slices(p.Mp, p.V));
   hipLaunchKernelGGL((k_head_wide<MT, KMAX>), grid, dim3(64 * HW_WAVES), 0, st, p);
   return hipGetLastError();
 }
@@ -314,11 +351,12 @@ hipError_t head_wide_mt(const HeadArgs& p, hipStream_t st) {
 #endif
 
 bool head_wide_ok(const HeadArgs& p) {
+  const size_t vpad = ((size_t)p.V + PACK_ROWS - 1) / PACK_ROWS * PACK_ROWS;
   return p.w_bf16 && p.w_packed && p.Mp >= DT_WIDE_MIN_MP && (p.Mp == 64 || p.Mp == 128) &&
-         p.d % (32 * HW_STEPS) == 0;
+         p.d % (32 * HW_STEPS) == 0 && vpad * (size_t)p.d * 2 < ((size_t)1 << 32);
 }
 
-int head_wide_tile_n() { return HW_TN; }
+int head_wide_slices(const HeadArgs& p) { return hw_slices(p.Mp, p.V); }
 
 hipError_t launch_head_wide(const HeadArgs& p, hipStream_t st) {
   switch (p.Mp) {

@@ -107,7 +107,7 @@ int head_tiles(const HeadArgs& h);           // vocabulary slices of this launch
 hipError_t launch_head(const HeadArgs& h, hipStream_t st);
 // 64/128-row packed bf16 variant (head_wide.hip); launch_head dispatches to it
 bool head_wide_ok(const HeadArgs& h);
-int head_wide_tile_n();
+int head_wide_slices(const HeadArgs& h);
 hipError_t launch_head_wide(const HeadArgs& h, hipStream_t st);
 // 128-row packed bf16 variant (head_rows128.hip): one vocabulary slice per
 // compute unit; launch_head prefers it over the 64/128-row one

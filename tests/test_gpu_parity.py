@@ -58,6 +58,15 @@ def small_cases():
     }
 
 
+def wide_vocab_cases():
+    # a vocabulary of 10001 tiles of 16 columns (ragged last tile): at 64 rows
+    # the wide head's slices hold 19-20 tiles (5 per wave, runs crossing the
+    # packed row groups); at 128 rows the 128-row head's slices of 19-20
+    # tiles of 32 columns
+    return {"bf16_wideV": synth.Workload("bf16_wideV", V=160001, d=256, wdtype="bf16", D=2, W=8,
+                                         k=8, B=16, beta=0.0, T=1.0, R=1, seeds=(23,))}
+
+
 _cache = {}
 
 
@@ -208,9 +217,13 @@ def test_build_is_deterministic(name, packed, R, W, multi_kernel):
     # the fp32 head at 16 and 32 rows (4 and 8 columns per thread)
     ("bf16_T1", 16, 16, 1.0, True), ("bf16_T1", 32, 4, 1.0, False),
     ("bf16_k16", 30, 16, 1.3, True), ("bf16_T1", 25, 1, 1.0, True),
-    ("tiny", 16, 8, 1.0, False), ("f32_wide", 30, 5, 1.0, False)])
+    ("tiny", 16, 8, 1.0, False), ("f32_wide", 30, 5, 1.0, False),
+    # a large vocabulary: the wide head at 64 rows (k = 8, greedy) and at 50
+    # rows padded to 64 with k = 16; the 128-row head
+    ("bf16_wideV", 64, 8, 1.0, True), ("bf16_wideV", 64, 1, 0.0, True),
+    ("bf16_wideV", 50, 16, 1.3, True), ("bf16_wideV", 128, 4, 0.8, True)])
 def test_corrected_topk_matches_oracle(name, rows, k, T, packed):
-    wl = small_cases()[name]
+    wl = {**small_cases(), **wide_vocab_cases()}[name]
     hw, _, head, ohead = case_inputs(wl, packed)
     tol, tau = tolerances(wl.wdtype)
     g = np.random.default_rng(rows * 31 + k)
