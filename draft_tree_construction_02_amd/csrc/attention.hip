@@ -493,20 +493,44 @@ __global__ void k_tree_attn_combine(AttnArgs a) {
   const int d4 = gid % (HD / 4);
   const int row = (gid / (HD / 4)) % nrows;
   const int g = gid / ((long)(HD / 4) * nrows);
+  // every split's (m, l) and partial output requested at once (one round
+  // trip), in groups of CMB_SPLITS
+  constexpr int CMB_SPLITS = 8;
   float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s)
-    M = fmaxf(M, a.mlpart[((long)s * a.Hkv + g) * nrows + row].x);
   f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  if (M != -INFINITY)
-    for (int s = 0; s < a.nsplit; ++s) {
-      const long b = ((long)s * a.Hkv + g) * nrows + row;
-      const float2 ml = a.mlpart[b];
-      const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-      const f32x4 v = *(const f32x4*)(a.opart + b * HD + 4 * d4);
-      num += w * v;
-      den += w * ml.y;
+  for (int s0 = 0; s0 < a.nsplit; s0 += CMB_SPLITS) {
+    float2 ml[CMB_SPLITS];
+    f32x4 v[CMB_SPLITS];
+#pragma unroll
+    for (int j = 0; j < CMB_SPLITS; ++j) {
+      ml[j] = make_float2(-INFINITY, 0.f);
+      v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s0 + j < a.nsplit) {
+        const long b = ((long)(s0 + j) * a.Hkv + g) * nrows + row;
+        ml[j] = a.mlpart[b];
+        v[j] = *(const f32x4*)(a.opart + b * HD + 4 * d4);
+      }
     }
+    // the group's largest m; earlier groups' sums are rescaled to it (with
+    // one group this is the plain sum against the global maximum)
+    float Mg = M;
+#pragma unroll
+    for (int j = 0; j < CMB_SPLITS; ++j) Mg = fmaxf(Mg, ml[j].x);
+    if (Mg == -INFINITY) continue;                   // no visible key so far
+    if (Mg > M && M != -INFINITY) {
+      const float c = __builtin_amdgcn_exp2f(M - Mg);
+      num *= c;
+      den *= c;
+    }
+    M = Mg;
+#pragma unroll
+    for (int j = 0; j < CMB_SPLITS; ++j) {
+      const float w = ml[j].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[j].x - M);
+      num += w * v[j];
+      den += w * ml[j].y;
+    }
+  }
   const int i = row / a.group, h = g * a.group + row % a.group;
   *(f32x4*)(a.out + ((long)i * a.Hq + h) * HD + 4 * d4) =
       den > 0.f ? num / den : f32x4{0.f, 0.f, 0.f, 0.f};
