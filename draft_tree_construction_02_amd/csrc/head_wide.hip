@@ -10,12 +10,11 @@
 // workgroups resident at once), at 128 rows runs of at most 16 tiles with 4
 // per wave.  A run may cross the packed layout's row groups, so every tile
 // has its own block offset; a wave's tiles past its slice re-read the
-// slice's last tile (in bounds, never reported).  The
-// weight fragments of the next 64-K chunk are requested right after the
-// MFMAs of the current one consume theirs, and the activation chunk is
-// double-buffered in LDS with a single barrier per chunk, so two waves per
-// SIMD keep both the HBM stream and the matrix cores busy.  Weights must be
-// in the packed layout (pack.hip).
+// slice's last tile (in bounds, never reported).  The weight fragments of the
+// next 64-K chunk are requested right after the MFMAs of the current one
+// consume theirs, and the activation chunk is double-buffered in LDS with a
+// single barrier per chunk, so two waves per SIMD keep both the HBM stream and
+// the matrix cores busy.  Weights must be in the packed layout (pack.hip).
 #include "common.hpp"
 #include "launch.hpp"
 
