@@ -63,8 +63,13 @@ def wide_vocab_cases():
     # the wide head's slices hold 19-20 tiles (5 per wave, runs crossing the
     # packed row groups); at 128 rows the 128-row head's slices of 19-20
     # tiles of 32 columns
+    # 12501 tiles of 16 at V = 200001 need more than two slices per compute
+    # unit at 64 rows (runs of 20 tiles, a second round) and more than one
+    # 128-row slice per compute unit
     return {"bf16_wideV": synth.Workload("bf16_wideV", V=160001, d=256, wdtype="bf16", D=2, W=8,
-                                         k=8, B=16, beta=0.0, T=1.0, R=1, seeds=(23,))}
+                                         k=8, B=16, beta=0.0, T=1.0, R=1, seeds=(23,)),
+            "bf16_hugeV": synth.Workload("bf16_hugeV", V=200001, d=128, wdtype="bf16", D=2, W=8,
+                                         k=8, B=16, beta=0.0, T=1.0, R=1, seeds=(24,))}
 
 
 _cache = {}
@@ -221,7 +226,8 @@ def test_build_is_deterministic(name, packed, R, W, multi_kernel):
     # a large vocabulary: the wide head at 64 rows (k = 8, greedy) and at 50
     # rows padded to 64 with k = 16; the 128-row head
     ("bf16_wideV", 64, 8, 1.0, True), ("bf16_wideV", 64, 1, 0.0, True),
-    ("bf16_wideV", 50, 16, 1.3, True), ("bf16_wideV", 128, 4, 0.8, True)])
+    ("bf16_wideV", 50, 16, 1.3, True), ("bf16_wideV", 128, 4, 0.8, True),
+    ("bf16_hugeV", 64, 8, 1.0, True), ("bf16_hugeV", 128, 8, 1.0, True)])
 def test_corrected_topk_matches_oracle(name, rows, k, T, packed):
     wl = {**small_cases(), **wide_vocab_cases()}[name]
     hw, _, head, ohead = case_inputs(wl, packed)
