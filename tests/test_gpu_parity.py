@@ -69,7 +69,11 @@ def wide_vocab_cases():
     return {"bf16_wideV": synth.Workload("bf16_wideV", V=160001, d=256, wdtype="bf16", D=2, W=8,
                                          k=8, B=16, beta=0.0, T=1.0, R=1, seeds=(23,)),
             "bf16_hugeV": synth.Workload("bf16_hugeV", V=200001, d=128, wdtype="bf16", D=2, W=8,
-                                         k=8, B=16, beta=0.0, T=1.0, R=1, seeds=(24,))}
+                                         k=8, B=16, beta=0.0, T=1.0, R=1, seeds=(24,)),
+            # 7 tiles of 16 (V = 100): one slice, waves 2 and 3 own only
+            # re-read tiles, wave 1 a ragged last tile
+            "bf16_tinyV": synth.Workload("bf16_tinyV", V=100, d=128, wdtype="bf16", D=2, W=8,
+                                         k=8, B=16, beta=0.0, T=1.0, R=1, seeds=(25,))}
 
 
 _cache = {}
@@ -227,7 +231,9 @@ def test_build_is_deterministic(name, packed, R, W, multi_kernel):
     # rows padded to 64 with k = 16; the 128-row head
     ("bf16_wideV", 64, 8, 1.0, True), ("bf16_wideV", 64, 1, 0.0, True),
     ("bf16_wideV", 50, 16, 1.3, True), ("bf16_wideV", 128, 4, 0.8, True),
-    ("bf16_hugeV", 64, 8, 1.0, True), ("bf16_hugeV", 128, 8, 1.0, True)])
+    ("bf16_hugeV", 64, 8, 1.0, True), ("bf16_hugeV", 128, 8, 1.0, True),
+    ("bf16_tinyV", 64, 8, 1.0, True), ("bf16_tinyV", 40, 16, 0.0, True),
+    ("bf16_tinyV", 128, 4, 1.0, True)])
 def test_corrected_topk_matches_oracle(name, rows, k, T, packed):
     wl = {**small_cases(), **wide_vocab_cases()}[name]
     hw, _, head, ohead = case_inputs(wl, packed)
