@@ -73,7 +73,11 @@ def wide_vocab_cases():
             # 7 tiles of 16 (V = 100): one slice, waves 2 and 3 own only
             # re-read tiles, wave 1 a ragged last tile
             "bf16_tinyV": synth.Workload("bf16_tinyV", V=100, d=128, wdtype="bf16", D=2, W=8,
-                                         k=8, B=16, beta=0.0, T=1.0, R=1, seeds=(25,))}
+                                         k=8, B=16, beta=0.0, T=1.0, R=1, seeds=(25,)),
+            # V = 20: one 32-column tile, so the second half of the 128-row
+            # head's slice has no tile at all and reports an empty part
+            "bf16_microV": synth.Workload("bf16_microV", V=20, d=128, wdtype="bf16", D=2, W=8,
+                                          k=4, B=16, beta=0.0, T=1.0, R=1, seeds=(26,))}
 
 
 _cache = {}
@@ -233,7 +237,9 @@ def test_build_is_deterministic(name, packed, R, W, multi_kernel):
     ("bf16_wideV", 50, 16, 1.3, True), ("bf16_wideV", 128, 4, 0.8, True),
     ("bf16_hugeV", 64, 8, 1.0, True), ("bf16_hugeV", 128, 8, 1.0, True),
     ("bf16_tinyV", 64, 8, 1.0, True), ("bf16_tinyV", 40, 16, 0.0, True),
-    ("bf16_tinyV", 128, 4, 1.0, True)])
+    ("bf16_tinyV", 128, 4, 1.0, True),
+    ("bf16_microV", 128, 4, 1.0, True), ("bf16_microV", 64, 4, 0.0, True),
+    ("bf16_microV", 16, 16, 0.7, True)])
 def test_corrected_topk_matches_oracle(name, rows, k, T, packed):
     wl = {**small_cases(), **wide_vocab_cases()}[name]
     hw, _, head, ohead = case_inputs(wl, packed)
