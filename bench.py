@@ -249,7 +249,16 @@ def main():
         log(f"[bench] step replayed from a HIP graph: {g_step:.3f} ms/step "
             f"(eager {ms_per_step:.3f})")
         del graph
+    def leg(name, fn):
+        # an extra measurement that fails is recorded in its field; the line still prints
+        try:
+            return fn()
+        except Exception as exc:          # noqa: BLE001 - recorded in the line, not hidden
+            log(f"[bench] {name} failed: {type(exc).__name__}: {exc}")
+            return {"error": f"{type(exc).__name__}: {exc}"[:300]}
+
     probe = hbm_probe(A, torch, dev)
+    mprobe = leg("matrix-core probe", lambda: mfma_probe(A, torch, dev))
     log(f"[bench] read probe: {probe['bytes'] / 2 ** 30:.0f} GiB in {probe['us']:.1f} us "
         f"-> {probe['gbs']:.0f} GB/s")
 
@@ -295,6 +304,7 @@ def main():
                      "probe_gbs": probe["gbs"],
                      "frac_of_probe": round(achieved / probe["gbs"], 4)},
         "hbm_probe": probe,
+        "mfma_probe": mprobe,
         "graph": graph_res,
         "step_ms": {"mean": round(ms_per_step, 4), "median": round(pct(per, 0.5), 4),
                     "p10": round(pct(per, 0.1), 4), "p90": round(pct(per, 0.9), 4)},
@@ -312,13 +322,6 @@ def main():
 
     # the extra legs below report beside the headline; if one of them fails,
     # the line still carries the measurement, with the failure in its field
-    def leg(name, fn):
-        try:
-            return fn()
-        except Exception as exc:          # noqa: BLE001 - recorded in the line, not hidden
-            log(f"[bench] {name} failed: {type(exc).__name__}: {exc}")
-            return {"error": f"{type(exc).__name__}: {exc}"[:300]}
-
     seq_tree = None
     if wl.R == 1 and not args.no_sequential:
         out = leg("sequential baseline", lambda: sequential_baseline(
@@ -334,6 +337,38 @@ def main():
         res["cpu_baseline"] = leg("cpu baseline", lambda: cpu_baseline(
             wl, hw, req, max(args.cpu_builds, wl.R), args.cpu_budget_s))
     print(json.dumps(res), flush=True)
+
+
+def mfma_probe(A, torch, dev, iters=297, reps=10):
+    """bf16 matrix-core rate with operands in registers, for operands that
+    are all 1.0 and for seeded N(0,1) operands: iters = 297 rounds are 9504
+    `32x32x16` products per SIMD, the 128-row head's hi/lo products per launch
+    at d = 4096, V = 151936.  Timed with events over `reps` calls; the constant
+    run's sums are checked exactly."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    n = cus * 32768
+    g = torch.Generator(device="cpu").manual_seed(5)
+    bufs = {"constant": torch.ones(n, dtype=torch.bfloat16, device=dev),
+            "random": torch.randn(n, generator=g).to(torch.bfloat16).to(dev)}
+    out = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    flop = cus * 8 * iters * 16 * 32768
+    res = {"products_per_simd": 2 * iters * 16, "flop_per_call": flop}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for name, buf in bufs.items():
+        for _ in range(2):
+            A.mfma_rate_probe(buf, iters, out=out)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            A.mfma_rate_probe(buf, iters, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        if name == "constant" and not bool(torch.all(out == 4096.0 * iters)):
+            raise RuntimeError("matrix-core probe returned a wrong sum")
+        res[name] = {"us": round(us, 2), "tflops": round(flop / (us * 1e-6) / 1e12, 1)}
+    del bufs
+    return res
 
 
 def hbm_probe(A, torch, dev, nbytes=2 << 30, reps=10):

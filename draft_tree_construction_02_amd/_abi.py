@@ -30,7 +30,7 @@ EXPORTS = [
     "build_tree_sequential_workspace_size", "build_tree_sequential",
     "prune_topB", "build_tree_mask",
     "tree_attention_workspace_size", "tree_attention_verify",
-    "accept_walk_workspace_size", "accept_walk", "hbm_read_probe",
+    "accept_walk_workspace_size", "accept_walk", "hbm_read_probe", "mfma_rate_probe",
     "dartree_timing_enable", "dartree_timing_reset", "dartree_timing_read",
 ]
 
@@ -96,6 +96,7 @@ def lib():
             "accept_walk": (i32, [hp, vp, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp, vp,
                                   vp, vp, vp, vp, sz, vp]),
             "hbm_read_probe": (i32, [vp, sz, vp, vp]),
+            "mfma_rate_probe": (i32, [vp, sz, i32, vp, sz, vp]),
             "dartree_timing_enable": (i32, [i32]),
             "dartree_timing_reset": (i32, []),
             "dartree_timing_read": (i32, [i32, C.POINTER(C.c_double), C.POINTER(C.c_int64)]),
@@ -448,6 +449,25 @@ def hbm_read_probe(buf, out=None, stream=None):
     _dev(out, torch.int64, "out", (1,))
     rc = lib().hbm_read_probe(_ptr(buf) if nbytes else None, nbytes, _ptr(out), _stream(stream))
     _check(rc, "hbm_read_probe")
+    return out
+
+
+def mfma_rate_probe(operands, iters, out=None, stream=None):
+    """bf16 matrix-core products with operands in registers (see the header):
+    `operands` a contiguous bf16 device tensor of at least cus * 32768
+    elements, `iters` rounds; returns the device float tensor of cus * 512
+    per-thread accumulator sums."""
+    if not isinstance(operands, torch.Tensor) or operands.device.type != "cuda":
+        raise ValueError("operands must be a device tensor")
+    if operands.dtype != torch.bfloat16 or not operands.is_contiguous():
+        raise ValueError("operands must be contiguous bfloat16")
+    cus = torch.cuda.get_device_properties(operands.device).multi_processor_count
+    if out is None:
+        out = torch.empty(cus * 512, dtype=torch.float32, device=operands.device)
+    _dev(out, torch.float32, "out", (cus * 512,))
+    rc = lib().mfma_rate_probe(_ptr(operands), operands.numel() * 2, int(iters), _ptr(out),
+                               out.numel(), _stream(stream))
+    _check(rc, "mfma_rate_probe")
     return out
 
 

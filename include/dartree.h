@@ -441,6 +441,27 @@ int accept_walk(const dt_head* target, const float* h, const float* s0,
  */
 int hbm_read_probe(const void* buf, size_t bytes, uint64_t* sum, void* stream);
 
+/*
+ * mfma_rate_probe - runs bf16 32x32x16 matrix-core products with operands held
+ * in registers, the bound of the corrected-logit head when its rows are many
+ * (its hi/lo products are 2 * 2 * rows * d * V flop per depth; at 128 rows
+ * they, not the weight stream of [P3] Summary & Methodology Analysis, set its
+ * time, and the product rate depends on the operand data).  One workgroup of
+ * 8 waves per compute unit (cus = the device's compute units); wave w of
+ * workgroup g holds 8 fragments of 1 KB from operands + (8 g + w) * 8 KB
+ * (4 weight-like, 4 activation-like bf16 tiles) and runs `iters` rounds of
+ * 16 products into 4 accumulators, then writes each thread's sum of its
+ * accumulators to out[512 g + thread].  With every operand 1.0 each output is
+ * exactly 4096 * iters.
+ *   operands  device bf16 buffer, 16-byte aligned, >= cus * 64 KB
+ *   bytes     its size in bytes
+ *   iters     rounds, >= 0 (cus * 8 * iters * 16 * 32768 flop per call)
+ *   out       device float[out_count], out_count >= cus * 512
+ * One launch on `stream`; DT_EINVAL on a NULL, misaligned or short buffer.
+ */
+int mfma_rate_probe(const void* operands, size_t bytes, int iters, float* out, size_t out_count,
+                    void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Kernel timing (off by default)                                            */
 /* ------------------------------------------------------------------------ */

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_every_declared_symbol_is_exported():
     names = header_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     L = A.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -291,6 +291,15 @@ def test_timing_api_without_launches():
     with pytest.raises(KeyError):
         A.timing_read("nope")
     assert A.lib().dartree_timing_read(9, C.byref(C.c_double()), C.byref(C.c_int64())) == DT_EINVAL
+
+
+def test_mfma_rate_probe_validation():
+    L = A.lib()
+    probe = L.mfma_rate_probe
+    assert probe(None, 1 << 30, 1, 1 << 20, 1 << 20, None) == DT_EINVAL          # no operands
+    assert probe(1 << 20, 1 << 30, 1, None, 1 << 20, None) == DT_EINVAL          # no output
+    assert probe((1 << 20) + 8, 1 << 30, 1, 1 << 21, 1 << 20, None) == DT_EINVAL  # misaligned
+    assert probe(1 << 20, 1 << 30, -1, 1 << 21, 1 << 20, None) == DT_EINVAL      # negative rounds
 
 
 def test_hbm_read_probe_validation():

@@ -2,7 +2,9 @@
 modulo 2^64, exactly as the oracle's definition gives it, for sizes from
 empty to the 2 GiB buffer the benchmark times: fewer 16-byte pieces than
 waves (waves with empty shares), a trailing 8-byte word, shares that end in
-a partial round of 16 loads, and many full rounds per wave."""
+a partial round of 16 loads, and many full rounds per wave.  The matrix-core
+rate probe gives 4096 per round per thread for operands of 1.0, and for random
+operands per-wave sums that satisfy the identity of a product's total."""
 import numpy as np
 import pytest
 import torch
@@ -46,3 +48,39 @@ def test_probe_on_benchmark_size_and_offsets():
         A.hbm_read_probe(buf[8:24])
     del buf
     torch.cuda.empty_cache()
+
+
+def _cus():
+    return torch.cuda.get_device_properties(DEV).multi_processor_count
+
+
+@pytest.mark.parametrize("iters", [0, 1, 10, 297])
+def test_mfma_probe_exact_on_ones(iters):
+    # every 32x32x16 product of ones adds 16 to each accumulator element; a
+    # round is 4 products per accumulator, 4 accumulators of 16 elements
+    print(f"matrix-core probe, ones, {iters} rounds", flush=True)
+    ops = torch.ones(_cus() * 32768, dtype=torch.bfloat16, device=DEV)
+    out = A.mfma_rate_probe(ops, iters)
+    torch.cuda.synchronize()
+    assert bool(torch.all(out == 4096.0 * iters))
+
+
+def test_mfma_probe_random_operands_total():
+    # the sum of all 32 x 32 outputs of a product A B is sum_k colsum(A)[k]
+    # rowsum(B)[k]; lane l of a fragment holds K index 8 (l / 32) + i in
+    # element i for both operands.  Per wave and round: sum over the 4 weight
+    # fragments and the 4 activation fragments of those dot products.
+    print("matrix-core probe, random operands", flush=True)
+    cus, iters = _cus(), 3
+    g = torch.Generator(device="cpu").manual_seed(21)
+    host = torch.randn(cus * 32768, generator=g).to(torch.bfloat16)
+    out = A.mfma_rate_probe(host.to(DEV), iters).cpu().numpy().astype(np.float64)
+    frag = host.float().numpy().astype(np.float64).reshape(cus * 8, 8, 64, 8)   # [wave][frag][lane][elem]
+    ksum = frag.reshape(cus * 8, 8, 2, 32, 8).sum(axis=3).reshape(cus * 8, 8, 16)  # [wave][frag][k]
+    want = iters * np.einsum("wk,wk->w", ksum[:, :4].sum(axis=1), ksum[:, 4:].sum(axis=1))
+    got = out.reshape(cus * 8, 64).sum(axis=1)
+    scale = iters * np.einsum("wk,wk->w", np.abs(ksum[:, :4]).sum(axis=1),
+                              np.abs(ksum[:, 4:]).sum(axis=1)) + 1.0
+    assert np.all(np.abs(got - want) <= 1e-4 * scale)
+    with pytest.raises(A.DartreeError):
+        A.mfma_rate_probe(host.to(DEV)[: 1024], 1)              # shorter than cus * 64 KB
