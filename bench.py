@@ -162,6 +162,16 @@ def main():
         # verification layer over request 0's pruned tree (rows >= n_sel are empty)
         A.tree_attention_verify(vq, vkp, vvp, vkt, vvt, mask[0], scale, workspace=aws, out=aout)
 
+    def leg(name, fn):
+        # an extra measurement that fails is recorded in its field; the line still prints
+        try:
+            return fn()
+        except Exception as exc:          # noqa: BLE001 - recorded in the line, not hidden
+            log(f"[bench] {name} failed: {type(exc).__name__}: {exc}")
+            return {"error": f"{type(exc).__name__}: {exc}"[:300]}
+
+    # the matrix-core probe once before any step (and once after the timed steps, below)
+    mprobe_before = leg("matrix-core probe", lambda: mfma_probe(A, torch, dev))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -249,16 +259,9 @@ def main():
         log(f"[bench] step replayed from a HIP graph: {g_step:.3f} ms/step "
             f"(eager {ms_per_step:.3f})")
         del graph
-    def leg(name, fn):
-        # an extra measurement that fails is recorded in its field; the line still prints
-        try:
-            return fn()
-        except Exception as exc:          # noqa: BLE001 - recorded in the line, not hidden
-            log(f"[bench] {name} failed: {type(exc).__name__}: {exc}")
-            return {"error": f"{type(exc).__name__}: {exc}"[:300]}
-
     probe = hbm_probe(A, torch, dev)
-    mprobe = leg("matrix-core probe", lambda: mfma_probe(A, torch, dev))
+    mprobe = {"before_steps": mprobe_before,
+              "after_steps": leg("matrix-core probe", lambda: mfma_probe(A, torch, dev))}
     log(f"[bench] read probe: {probe['bytes'] / 2 ** 30:.0f} GiB in {probe['us']:.1f} us "
         f"-> {probe['gbs']:.0f} GB/s")
 
@@ -344,7 +347,8 @@ def mfma_probe(A, torch, dev, iters=297, reps=10):
     are all 1.0 and for seeded N(0,1) operands: iters = 297 rounds are 9504
     `32x32x16` products per SIMD, the 128-row head's hi/lo products per launch
     at d = 4096, V = 151936.  Timed with events over `reps` calls; the constant
-    run's sums are checked exactly."""
+    run's sums are checked exactly.  The bench runs it before the warm-up steps
+    and after the timed steps: the rate depends on the part's state."""
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     n = cus * 32768
     g = torch.Generator(device="cpu").manual_seed(5)
